@@ -1,0 +1,274 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test checks the oracle against something other than itself: a closed
+form evaluated through a different route (SVD + scalar iteration), a textbook
+special case (the classical Newton-Schulz polar iteration), an invariant of
+the Hyperball step [arXiv §3.3, Eq. (1)], or a value printed on the pages.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import muonh as om
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+A, B, C = oracle.NS_COEFFS_QUINTIC
+
+
+def _scalar_iter(x, steps=5, coeffs=oracle.NS_COEFFS_QUINTIC):
+    a, b, c = coeffs
+    for _ in range(steps):
+        x = a * x + b * x ** 3 + c * x ** 5
+    return x
+
+
+def _svd_closed_form(y, steps=5, coeffs=oracle.NS_COEFFS_QUINTIC, eps=1e-7):
+    """An odd matrix polynomial acts on singular values only:
+    NS(Y) = U diag(p^(steps)(sigma / (||Y||_F + eps))) V^T."""
+    u, s, vt = np.linalg.svd(y, full_matrices=False)
+    scale = np.linalg.norm(y) + eps
+    return (u * _scalar_iter(s / scale, steps, coeffs)) @ vt
+
+
+def _rel(a, b):
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+def _with_singular_values(rng, r, c, s):
+    u, _ = np.linalg.qr(rng.standard_normal((r, len(s))))
+    v, _ = np.linalg.qr(rng.standard_normal((c, len(s))))
+    return (u * np.asarray(s)) @ v.T
+
+
+@pytest.mark.parametrize("shape", [(8, 5), (5, 8), (64, 16), (16, 64), (33, 33), (3, 40)])
+def test_ns_matches_svd_closed_form(shape):
+    rng = np.random.default_rng(1)
+    y = rng.standard_normal(shape)
+    got = oracle.newton_schulz(y)
+    assert _rel(got, _svd_closed_form(y)) <= 1e-10
+
+
+def test_ns_rank_deficient_and_repeated_sigma():
+    rng = np.random.default_rng(2)
+    y = _with_singular_values(rng, 12, 9, [3.0, 1.0, 0.2])           # rank 3
+    assert _rel(oracle.newton_schulz(y), _svd_closed_form(y)) <= 1e-10
+    y = _with_singular_values(rng, 10, 20, [2.0, 2.0, 2.0, 0.5, 0.5])  # repeated
+    assert _rel(oracle.newton_schulz(y), _svd_closed_form(y)) <= 1e-10
+
+
+def test_ns_singular_vectors_and_band():
+    """Output shares the input's singular vectors, and every singular value
+    whose normalised input is >= 2e-3 lands in the band the five-fold scalar
+    quintic gives: [0.68183, 1.20237] (>= 5e-3: upper edge 1.15437)."""
+    rng = np.random.default_rng(3)
+    y = rng.standard_normal((48, 96))
+    o = oracle.newton_schulz(y)
+    u, s, vt = np.linalg.svd(y, full_matrices=False)
+    core = u.T @ o @ vt.T
+    off = core - np.diag(np.diag(core))
+    assert np.linalg.norm(off) <= 1e-10 * np.linalg.norm(o)
+    xs = np.geomspace(2e-3, 1.0, 200001)
+    ys = _scalar_iter(xs)
+    lo, hi = ys.min(), ys.max()
+    assert abs(lo - 0.68183) < 1e-5 and abs(hi - 1.20237) < 1e-5
+    sig_in = s / (np.linalg.norm(y) + 1e-7)
+    sig_out = np.diag(core)
+    mask = sig_in >= 2e-3
+    assert mask.all()
+    assert np.all(sig_out[mask] >= lo - 1e-12) and np.all(sig_out[mask] <= hi + 1e-12)
+
+
+def test_ns_classical_coefficients_give_polar_factor():
+    """Classical Newton-Schulz (15/8, -10/8, 3/8) converges to U V^T, the
+    polar factor from the SVD, on a well-conditioned matrix."""
+    rng = np.random.default_rng(4)
+    y = _with_singular_values(rng, 7, 11, [5.0, 3.0, 2.0, 1.0, 0.6, 0.4, 0.2])
+    o = oracle.newton_schulz(y, steps=40, coeffs=oracle.NS_COEFFS_CLASSICAL)
+    u, _, vt = np.linalg.svd(y, full_matrices=False)
+    assert _rel(o, u @ vt) <= 1e-12
+
+
+def test_ns_orientation_is_exact():
+    rng = np.random.default_rng(5)
+    y = rng.standard_normal((40, 9))
+    assert _rel(oracle.newton_schulz(y, orient=True), oracle.newton_schulz(y, orient=False)) <= 1e-12
+
+
+def test_rank_one_update_direction():
+    """Y = s x y^T has one singular value, so u_hat = x y^T exactly and
+    W~ = W - eta R x y^T."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal(13); x /= np.linalg.norm(x)
+    z = rng.standard_normal(7); z /= np.linalg.norm(z)
+    g = 4.0 * np.outer(x, z)
+    w0 = rng.standard_normal((13, 7))
+    st = oracle.OracleMatrixState.from_arrays(w0)
+    us, diags, _ = oracle.muonh_step([st], [g], eta=0.05)
+    u_hat = us[0] / np.linalg.norm(us[0])
+    assert _rel(u_hat, np.outer(x, z)) <= 1e-12
+    wt = w0 - 0.05 * st.R * np.outer(x, z)
+    assert _rel(st.w, st.R * wt / np.linalg.norm(wt)) <= 1e-12
+
+
+def test_momentum_closed_form():
+    rng = np.random.default_rng(7)
+    beta = 0.95
+    gs = [rng.standard_normal((6, 4)) for _ in range(5)]
+    st = oracle.OracleMatrixState.from_arrays(rng.standard_normal((6, 4)))
+    for g in gs:
+        oracle.muonh_step([st], [g], eta=0.01, opts=oracle.OracleOptions(beta=beta))
+    t = len(gs) - 1
+    expect = sum(beta ** (t - k) * gs[k] for k in range(len(gs)))
+    assert _rel(st.m, expect) <= 1e-14
+
+
+def test_nesterov_iterate():
+    """With Nesterov the Newton-Schulz input is G + beta*M_new; on the first
+    step (M_0 = 0) that is (1 + beta) G, the same direction as G."""
+    rng = np.random.default_rng(8)
+    g = rng.standard_normal((9, 5))
+    st1 = oracle.OracleMatrixState.from_arrays(np.ones((9, 5)))
+    st2 = oracle.OracleMatrixState.from_arrays(np.ones((9, 5)))
+    u1, _, _ = oracle.muonh_step([st1], [g], 0.01, oracle.OracleOptions(nesterov=True, ns_eps=0.0))
+    u2, _, _ = oracle.muonh_step([st2], [g], 0.01, oracle.OracleOptions(nesterov=False, ns_eps=0.0))
+    assert _rel(u1[0], u2[0]) <= 1e-13
+    g2 = rng.standard_normal((9, 5))
+    u1, _, _ = oracle.muonh_step([st1], [g2], 0.01, oracle.OracleOptions(nesterov=True, ns_eps=0.0))
+    y = g2 + 0.95 * (0.95 * g + g2)
+    assert _rel(u1[0], _svd_closed_form(y, eps=0.0)) <= 1e-10
+
+
+def test_hyperball_invariant_elr_and_angle():
+    """||W_{t+1}|| = R after every step; the pre-projection displacement is
+    eta R, so the effective LR is eta [arXiv §3.3.1]; the angle turned equals
+    the chord angle 2 asin(||dW|| / 2R) and cos(theta) = <W_t, W_{t+1}> / R^2."""
+    rng = np.random.default_rng(9)
+    w0 = rng.standard_normal((24, 40))
+    w0 *= math.sqrt(24) / np.linalg.norm(w0)
+    st = oracle.OracleMatrixState.from_arrays(w0)
+    for k in range(8):
+        eta = 0.012 * (1 - k / 20)
+        w_prev = st.w.copy()
+        g = rng.standard_normal((24, 40)) + 0.3 * w_prev   # correlated with W: c != 0
+        _, diags, _ = oracle.muonh_step([st], [g], eta)
+        d = diags[0]
+        assert abs(np.linalg.norm(st.w) / st.R - 1.0) <= 1e-14
+        assert abs(d.elr - eta) <= 1e-12 * eta
+        theta_chord = oracle.chord_angle(w_prev, st.w, st.R)
+        cos_t = float(np.sum(w_prev * st.w)) / st.R ** 2
+        assert abs(theta_chord - d.angle) <= 1e-9 * eta
+        assert abs(math.acos(min(1.0, cos_t)) - d.angle) <= 1e-6 * eta
+        assert abs(d.angle - eta) <= eta * (abs(d.c) + eta)
+
+
+def test_scale_invariance():
+    """Scaling every gradient of a matrix by a positive constant leaves the
+    trajectory unchanged (exactly with eps = 0; the 1/sqrt(fan_in) scaling of
+    the 170M workload is such a constant)."""
+    rng = np.random.default_rng(10)
+    w0 = rng.standard_normal((16, 48))
+    gs = [rng.standard_normal((16, 48)) for _ in range(4)]
+    for eps, tol in ((0.0, 1e-12), (1e-7, 1e-6)):
+        opts = oracle.OracleOptions(ns_eps=eps)
+        s1 = oracle.OracleMatrixState.from_arrays(w0)
+        s2 = oracle.OracleMatrixState.from_arrays(w0)
+        for g in gs:
+            oracle.muonh_step([s1], [g], 0.02, opts)
+            oracle.muonh_step([s2], [g / math.sqrt(48)], 0.02, opts)
+        assert _rel(s2.w, s1.w) <= tol
+
+
+def test_zero_gradient_is_projection_only():
+    w0 = np.arange(12.0).reshape(3, 4) + 1.0
+    st = oracle.OracleMatrixState.from_arrays(w0, R=5.0)
+    us, diags, _ = oracle.muonh_step([st], [np.zeros((3, 4))], 0.1)
+    assert np.all(us[0] == 0.0)
+    assert _rel(st.w, 5.0 * w0 / np.linalg.norm(w0)) <= 1e-15
+
+
+def test_nonfinite_propagates():
+    g = np.ones((4, 4)); g[1, 2] = np.nan
+    st = oracle.OracleMatrixState.from_arrays(np.eye(4))
+    _, diags, _ = oracle.muonh_step([st], [g], 0.1)
+    assert diags[0].nonfinite and np.isnan(st.w).all()
+
+
+def test_muon_wd_and_elr_aligned():
+    """Eq. (3): W_{t+1} + eta u = (1 - lambda eta) W_t.  Eq. (5): the aligned
+    LR makes the measured relative displacement ||dW|| / ||W_t|| equal rho."""
+    rng = np.random.default_rng(11)
+    w = rng.standard_normal((10, 30))
+    u = oracle.newton_schulz(rng.standard_normal((10, 30)))
+    w1 = oracle.muon_wd_update(w, u, 0.02, 0.1)
+    assert _rel(w1 + 0.02 * u, (1 - 0.002) * w) <= 1e-15
+    w2, eta_t = oracle.elr_aligned_update(w, u, 0.013)
+    assert abs(np.linalg.norm(w2 - w) / np.linalg.norm(w) - 0.013) <= 1e-14
+    assert eta_t > 0
+
+
+def test_dense_flops_formula():
+    # 1.7B down projection 2048 x 6144: 5 x (4 m^2 n + 2 m^3)
+    assert om.ns_dense_flops(2048, 6144) == 5 * (4 * 2048 ** 2 * 6144 + 2 * 2048 ** 3)
+    assert om.ns_dense_flops(6144, 2048) == om.ns_dense_flops(2048, 6144)
+
+
+# ---------------------------------------------------------------------------
+# schedule values printed on the pages
+
+with open(os.path.join(HERE, "golden", "schedule_pins.json")) as f:
+    PINS = json.load(f)
+
+
+def _printed_match(value, printed):
+    """Equal at the printed precision (3 significant figures)."""
+    return float(f"{value:.3g}") == printed
+
+
+def test_phase1_power_schedule_end_and_peak():
+    tps = PINS["tokens_per_step"]
+    p = PINS["phase1_end"]
+    k = p["tokens"] / tps
+    v = oracle.lr_phase1_power(k)
+    assert _printed_match(v, p["printed_base_lr"])
+    assert _printed_match(oracle.hyperball_lr(v), p["printed_hyperball_lr"])
+    w = PINS["phase1_warmup_peak"]
+    assert oracle.lr_phase1_power(w["step"]) == pytest.approx(w["printed_base_lr"], rel=1e-15)
+    assert oracle.lr_phase1_power(w["step"] + 1e-9) == pytest.approx(w["printed_base_lr"], rel=1e-9)
+    assert oracle.lr_phase1_power(500) == pytest.approx(2.5e-3, rel=1e-15)
+
+
+def test_phase2_linear_and_cma_hold():
+    tps = PINS["tokens_per_step"]
+    eta0 = oracle.lr_phase1_power(PINS["phase1_end"]["tokens"] / tps)
+    h = PINS["cma_hold"]
+    S = h["run_last_step"] - h["phase2_start_step"]
+
+    def sched(k):
+        return oracle.lr_linear(eta0, h["eta_min"], k - h["phase2_start_step"], S)
+
+    v = oracle.lr_constant_hold(220000, h["hold_step"], sched)
+    assert _printed_match(v, h["printed_base_lr"])
+    assert _printed_match(oracle.hyperball_lr(v), h["printed_hyperball_lr"])
+    assert sched(h["phase2_start_step"]) == eta0
+    assert sched(h["run_last_step"]) == pytest.approx(h["eta_min"], rel=1e-12)
+    w = PINS["cma_window"]
+    assert round((h["run_last_step"] - h["hold_step"]) * tps / 1e9) == w["printed_last_tokens_B"]
+    assert round((h["run_last_step"] - 222100) * tps / 1e9, 2) == w["printed_window_tokens_B"]
+    assert h["run_last_step"] - 222100 == w["printed_window_steps"]
+    assert round(w["printed_spacing_steps"] * tps / 1e9, 2) == w["printed_spacing_tokens_B"]
+
+
+def test_wsd_and_cosine_shapes():
+    assert oracle.lr_wsd(0, 0.024, 10, 1.0) == pytest.approx(0.024)
+    assert oracle.lr_wsd(5, 0.024, 10, 1.0) == pytest.approx(0.012)
+    assert oracle.lr_wsd(10, 0.024, 10, 1.0) == 0.0
+    assert oracle.lr_wsd(3, 0.01, 10, 0.5) == 0.01
+    assert oracle.lr_wsd(7.5, 0.01, 10, 0.5) == pytest.approx(0.005)
+    assert oracle.lr_cosine(0, 100, 1e-5, 1e-7) == pytest.approx(1e-5)
+    assert oracle.lr_cosine(50, 100, 1e-5, 1e-7) == pytest.approx(0.5 * (1e-5 + 1e-7))
+    assert oracle.lr_cosine(100, 100, 1e-5, 1e-7) == pytest.approx(1e-7)
