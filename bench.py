@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the MuonH optimizer step on one MI355X.
+
+A "step" is one full MuonH step (momentum + pack, 5 quintic Newton-Schulz
+iterations on the grouped MFMA GEMM engine, reductions, Hyperball update)
+over every matrix of the workload, with weights, momenta and gradients
+resident in HBM.  Default workload: the 196 Qwen3-1.7B-shaped matrices
+(28 layers x q, k, v, o, gate, up, down), fp32 W and M, bf16 gradients,
+bf16 Newton-Schulz operands with fp32 accumulation.
+
+Prints ONE JSON line on stdout; a human-readable breakdown goes to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MuonH optimizer steps/sec on Qwen3-1.7B weights; NS MFMA util; elementwise HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def per_kernel_work(shapes, ns_steps, tsize, gsize):
+    """Algorithmic FLOP / bytes of each kernel family for one step.
+
+    NS products per matrix and iteration (m = min side, n = max side):
+      X X^T: 2 m^2 n,  A A: 2 m^3,  B X: 2 m^2 n  (dense counts).
+    Elementwise bytes per matrix (p = rows*cols, padded NS area q = m_pad*n_pad):
+      momentum: read G (gsize p) + read/write M (8 p) + write X_0 and X_0^T (2 tsize q)
+      reduce:   read W (4 p) + read u (tsize p)
+      update:   read/write W (8 p) + read u (tsize p)
+    """
+    def pad(x):
+        return (x + 255) // 256 * 256
+    f = {"ns_gram": 0.0, "ns_poly": 0.0, "ns_apply": 0.0}
+    b = {"momentum": 0.0, "reduce": 0.0, "update": 0.0}
+    params = 0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        f["ns_gram"] += ns_steps * 2.0 * m * m * n
+        f["ns_poly"] += ns_steps * 2.0 * m * m * m
+        f["ns_apply"] += ns_steps * 2.0 * m * m * n
+        p = r * c
+        q = pad(m) * pad(n)
+        params += p
+        b["momentum"] += gsize * p + 8 * p + 2 * tsize * q
+        b["reduce"] += 4 * p + tsize * p
+        b["update"] += 8 * p + tsize * p
+    return f, b, params
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def cpu_baseline(wl, ws_dev, grads_dev, eta, layer_mats: int):
+    """The CPU oracle (fp64 NumPy, as it stands) on one step of the first
+    `layer_mats` matrices, scaled to the whole set by FLOP share."""
+    import numpy as np
+    import inputs
+    import oracle
+    idx = list(range(layer_mats))
+    states = [oracle.OracleMatrixState.from_arrays(inputs.to_numpy64(ws_dev[i])) for i in idx]
+    gs = [inputs.to_numpy64(grads_dev[i]) for i in idx]
+    t0 = time.perf_counter()
+    oracle.muonh_step(states, gs, eta)
+    dt = time.perf_counter() - t0
+    from oracle.muonh import ns_dense_flops
+    share = sum(ns_dense_flops(*wl.shapes[i]) for i in idx) / sum(ns_dense_flops(*s) for s in wl.shapes)
+    full = dt / share
+    return {"value": 1.0 / full, "unit": "steps/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"one oracle step (fp64 NumPy) over matrices 0-{layer_mats - 1} "
+                      f"({share:.4f} of the step's Newton-Schulz FLOP) took {dt:.2f} s; "
+                      f"scaled by FLOP share to {full:.1f} s per full step",
+            "seconds_sample": dt, "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_1.7b")
+    ap.add_argument("--ns-dtype", choices=("bf16", "f32"), default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-mats", type=int, default=7,
+                    help="matrices the CPU oracle times (default: one layer)")
+    ap.add_argument("--grad-sets", type=int, default=4)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the step is not sharded across GPUs.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import inputs
+    import pretraining_optimizer_amd as pm
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = inputs.workload(args.workload)
+    ns = args.ns_dtype or wl.ns_dtype
+    log(f"workload {wl.name}: {len(wl.shapes)} matrices, {wl.params() / 1e9:.3f} G params, ns {ns}")
+
+    ws = [inputs.make_weight(wl, i, dev) for i in range(len(wl.shapes))]
+    ms = [torch.zeros_like(w) for w in ws]
+    nsets = max(1, min(args.grad_sets, args.warmup + args.steps))
+    pool = [[inputs.make_grad(wl, k, i, dev) for i in range(len(wl.shapes))] for k in range(nsets)]
+    torch.cuda.synchronize()
+    cpu_inputs = None
+    if not args.no_cpu_baseline:
+        # keep the step-0 inputs of the sampled matrices for the oracle
+        cpu_inputs = ([w.clone() for w in ws[:args.cpu_mats]], pool[0][:args.cpu_mats])
+
+    opt = pm.MuonH(ws, ms, grad_dtype=wl.g_dtype,
+                   ns_dtype=pm.MUONH_BF16 if ns == "bf16" else pm.MUONH_F32)
+    info = pm.plan_query(wl.shapes, pm.default_options(
+        ns_dtype=pm.MUONH_BF16 if ns == "bf16" else pm.MUONH_F32), g_dtype=opt._gcode)
+    S = opt.options.ns_steps
+    for k in range(args.warmup):
+        opt.step(pool[k % nsets], wl.eta(k % wl.steps), step=k)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    opt.set_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        kk = args.warmup + k
+        opt.step(pool[kk % nsets], wl.eta(kk % wl.steps), step=kk)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    phases, nt = opt.timing()
+    opt.set_timing(False)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    steps_per_s = args.steps / (t1 - t0)
+    stats = opt.stats()
+    R = opt.radii()
+    norm_dev = max(abs(torch.linalg.vector_norm(w.double()).item() / R[i] - 1.0)
+                   for i, w in enumerate(ws))
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {steps_per_s:.2f} steps/s; "
+        f"max | |W|/R - 1 | = {norm_dev:.2e}; any nonfinite: {any(s['nonfinite'] for s in stats)}")
+
+    tsize = 2 if ns == "bf16" else 4
+    gsize = 2 if wl.g_dtype == torch.bfloat16 else 4
+    flops, bytes_, params = per_kernel_work(wl.shapes, S, tsize, gsize)
+    per_step = {k: v / nt for k, v in phases.items()}
+    peak = PEAK_BF16_TFLOPS if ns == "bf16" else PEAK_F32_TFLOPS
+    kern = {}
+    for k in ("ns_gram", "ns_poly", "ns_apply"):
+        t_launch = per_step[k] / S
+        tf = flops[k] / S / (t_launch * 1e-3) / 1e12
+        kern[k] = {"ms_per_launch": t_launch, "dense_tflops": tf, "frac_of_peak": tf / peak}
+    for k in ("momentum", "reduce", "update"):
+        gbs = bytes_[k] / (per_step[k] * 1e-3) / 1e9
+        kern[k] = {"ms": per_step[k], "gbs": gbs, "frac_of_hbm": gbs / PEAK_HBM_GBS}
+    ns_ms = sum(per_step[k] for k in ("ns_gram", "ns_poly", "ns_apply"))
+    el_ms = sum(per_step[k] for k in ("momentum", "reduce", "update"))
+    ns_tflops = info.ns_dense_flops / (ns_ms * 1e-3) / 1e12
+    el_gbs = sum(bytes_.values()) / (el_ms * 1e-3) / 1e9
+    alg_gbs = info.elem_bytes / (el_ms * 1e-3) / 1e9
+    for k, v in per_step.items():
+        log(f"  {k:9s} {v:8.3f} ms/step  {kern[k]}")
+    log(f"  NS total {ns_ms:.3f} ms: {ns_tflops:.1f} dense TFLOP/s ({ns_tflops / peak:.1%} of peak); "
+        f"elementwise {el_ms:.3f} ms: {el_gbs:.0f} GB/s kernel bytes, {alg_gbs:.0f} GB/s at 18 B/param")
+
+    dom = max(("ns_gram", "ns_poly", "ns_apply"), key=lambda k: per_step[k])
+    roof = {"bound": "mfma", "achieved": kern[dom]["dense_tflops"], "peak": peak, "unit": "TFLOP/s",
+            "frac": kern[dom]["dense_tflops"] / peak, "traffic": None,
+            "kernel": {"ns_gram": "gemm_kernel<bf16, kGram> (X X^T)",
+                       "ns_poly": "gemm_kernel<bf16, kPoly> (b A + c A A)",
+                       "ns_apply": "gemm_kernel<bf16, kApply> (a X + B X)"}[dom],
+            "flop_per_launch": flops[dom] / S, "ms_per_launch": kern[dom]["ms_per_launch"]}
+
+    cpu = None
+    if cpu_inputs is not None:
+        log(f"cpu baseline: oracle on {args.cpu_mats} matrices ...")
+        cpu = cpu_baseline(wl, cpu_inputs[0], cpu_inputs[1], wl.eta(0), args.cpu_mats)
+        log(f"  {cpu['sample']}; {cpu['value']:.5f} steps/s on {cpu['cores']} BLAS threads")
+
+    out = {
+        "metric": METRIC, "value": steps_per_s, "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": ns, "data": "synthetic (seeded N(0,1) grads, W at radius sqrt(rows))",
+        "config": {"workload": f"{wl.name}: {len(wl.shapes)} matrices, {params} params, fp32 W/M, "
+                               f"{'bf16' if gsize == 2 else 'fp32'} grads, {ns} Newton-Schulz x{S}",
+                   "matrices": len(wl.shapes), "params": params, "parallelism": "single-gpu"},
+        "roofline": roof,
+        "ns_dense_tflops": ns_tflops, "ns_frac_of_peak": ns_tflops / peak,
+        "ns_exec_tflop_per_step": info.ns_exec_flops / 1e12,
+        "ns_dense_tflop_per_step": info.ns_dense_flops / 1e12,
+        "elementwise_gbs": el_gbs, "elementwise_frac_of_hbm": el_gbs / PEAK_HBM_GBS,
+        "elementwise_alg18_gbs": alg_gbs,
+        "kernels": kern, "phase_ms_per_step": per_step, "timed_steps_events": nt,
+        "norm_invariant_max_dev": norm_dev,
+        "cpu_baseline": cpu,
+    }
+    opt.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,21 @@
+"""MI355X (gfx950) MuonH optimizer step: HIP kernels behind a C ABI.
+
+The library (libmuonh.so, built from csrc/ by ``build.py``) runs momentum,
+quintic Newton-Schulz on a grouped bf16/fp32 MFMA GEMM engine and the
+Hyperball update of Eq. (1) of "Puro-2B: Poor Lab's Qwen2-1.5B Trained on
+RTX 5090 within $5090" (arXiv HTML §3.3).  ``muonh`` is its ctypes binding.
+"""
+
+from .muonh import (  # noqa: F401
+    MuonH,
+    MuonHError,
+    default_options,
+    load_library,
+    plan_query,
+    workspace_size,
+    MUONH_BF16,
+    MUONH_F32,
+    MUONH_MODE_HYPERBALL,
+    MUONH_MODE_MUON_WD,
+    MUONH_MODE_ELR_ALIGNED,
+)

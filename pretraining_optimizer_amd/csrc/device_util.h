@@ -1,0 +1,72 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 conversion and
+// 4-wide vector access to bf16 / fp32 buffers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muonh {
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// Global-memory (address space 1) access: pointers read from descriptor
+// tables are generic, and generic accesses compile to flat_* instructions,
+// which also count against the LDS wait counter.
+#define MUONH_GLOBAL __attribute__((address_space(1)))
+
+template <typename V>
+__device__ __forceinline__ V ld_global(const void* p) {
+  return *(const MUONH_GLOBAL V*)(p);  // C-style cast: generic -> global address space
+}
+template <typename V>
+__device__ __forceinline__ void st_global(void* p, V v) {
+  *(MUONH_GLOBAL V*)(p) = v;
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                                               // round to nearest even
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+// 4 consecutive elements of type T <-> 4 floats.
+template <typename T> struct Vec4;
+template <> struct Vec4<uint16_t> {
+  static __device__ __forceinline__ f32x4_t load(const uint16_t* p) {
+    const u32x2_t v = ld_global<u32x2_t>(p);
+    f32x4_t r;
+    r[0] = __uint_as_float(v[0] << 16);
+    r[1] = __uint_as_float(v[0] & 0xffff0000u);
+    r[2] = __uint_as_float(v[1] << 16);
+    r[3] = __uint_as_float(v[1] & 0xffff0000u);
+    return r;
+  }
+  static __device__ __forceinline__ void store(uint16_t* p, f32x4_t v) {
+    u32x2_t o;
+    o[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    o[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    st_global<u32x2_t>(p, o);
+  }
+  static __device__ __forceinline__ void store1(uint16_t* p, float v) {
+    st_global<uint16_t>(p, f32_to_bf16(v));
+  }
+};
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ f32x4_t load(const float* p) {
+    return ld_global<f32x4_t>(p);
+  }
+  static __device__ __forceinline__ void store(float* p, f32x4_t v) {
+    st_global<f32x4_t>(p, v);
+  }
+  static __device__ __forceinline__ void store1(float* p, float v) { st_global<float>(p, v); }
+};
+
+}  // namespace muonh

@@ -1,0 +1,413 @@
+// Fused, coalesced elementwise / reduction kernels of the MuonH step (gfx950).
+//
+// The step around the Newton-Schulz products is memory-bound streaming work:
+//   momentum_kernel : M <- beta M + G, Y = M (or G + beta M), partial ||Y||^2,
+//                     Y packed as the first iterate X_0 in BOTH layouts the
+//                     grouped GEMM reads (X and X^T), zero-padded;
+//   reduce_kernel   : <W,u>, ||u||^2, ||W||^2 partials;
+//   update_kernel   : W <- k1 W - k2 u  (Hyperball: k1 = R/||W~||,
+//                     k2 = k1 eta R / ||u||, from the closed form
+//                     ||W~||^2 = ||W||^2 - 2 k <W,u> + k^2 ||u||^2, k = eta R/||u||,
+//                     so W~ is never materialised)
+// plus one-wavefront-per-matrix finalise kernels.  The Hyperball step is
+// Eq. (1) of "Puro-2B: Poor Lab's Qwen2-1.5B Trained on RTX 5090 within
+// $5090" (arXiv HTML §3.3); the ordinary-Muon and ELR-aligned updates are its
+// Eqs. (3) and (5) (§3.3.1).
+//
+// Reductions are deterministic: per-thread fp32 sums over a fixed set of
+// elements, fp64 wavefront shuffles and an fp64 LDS tree in a fixed order,
+// per-block partials summed in block order by the finalise kernels.  No
+// floating-point atomics.
+
+#include <math.h>
+
+#include "device_util.h"
+#include "internal.h"
+
+namespace muonh {
+namespace {
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Sum of one double per thread over a 256-thread block; result valid in thread 0.
+template <int NV>
+__device__ __forceinline__ void block_sum(double (&v)[NV], double (*red)[4]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const double s = wave_sum(v[k]);
+    if (lane == 0) red[k][wave] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] = (red[k][0] + red[k][1]) + (red[k][2] + red[k][3]);
+  }
+}
+
+template <typename G> struct GradLoad;
+template <> struct GradLoad<uint16_t> {
+  static __device__ __forceinline__ f32x4_t load4(const void* p, int64_t off) {
+    return Vec4<uint16_t>::load(reinterpret_cast<const uint16_t*>(p) + off);
+  }
+  static __device__ __forceinline__ float load1(const void* p, int64_t off) {
+    return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[off]);
+  }
+};
+template <> struct GradLoad<float> {
+  static __device__ __forceinline__ f32x4_t load4(const void* p, int64_t off) {
+    return Vec4<float>::load(reinterpret_cast<const float*>(p) + off);
+  }
+  static __device__ __forceinline__ float load1(const void* p, int64_t off) {
+    return reinterpret_cast<const float*>(p)[off];
+  }
+};
+
+// ---------------------------------------------------------------------------
+// momentum + pack.  One 64 x 64 tile of the padded, original-orientation grid
+// per block; thread (rr, cc) handles rows rr + 16q, columns cc..cc+3.
+
+template <typename T, typename G>
+__device__ __forceinline__ void momentum_tile(const MomTile& t, const MatGeom& g, const MatPtrs& p,
+                                              double* partials, const ElemParams& prm,
+                                              float (*tile)[kMomTile + 1], double (*red)[4]) {
+  const int tid = threadIdx.x;
+  const int cc = (tid & 15) * 4;
+  const int rr = tid >> 4;
+  const int64_t r0 = (int64_t)t.tr * kMomTile, c0 = (int64_t)t.tc * kMomTile;
+  T* D = reinterpret_cast<T*>(g.tall ? g.XT[0] : g.X[0]);   // same orientation as M
+  T* Tr = reinterpret_cast<T*>(g.tall ? g.X[0] : g.XT[0]);  // transposed
+  const int64_t ldD = g.c_pad, ldT = g.r_pad;
+  const bool vec_ok = (g.cols & 3) == 0;
+  const float beta = prm.beta;
+  float ss = 0.0f;
+
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t row = r0 + rr + 16 * q;
+    const int64_t col = c0 + cc;
+    f32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (row < g.rows) {
+      const int64_t off = row * g.cols + col;
+      if (vec_ok && col + 3 < g.cols) {
+        const f32x4_t gv = GradLoad<G>::load4(p.g, off);
+        f32x4_t mv = Vec4<float>::load(p.m + off);
+        mv = beta * mv + gv;
+        Vec4<float>::store(p.m + off, mv);
+        y = prm.nesterov ? gv + beta * mv : mv;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (col + e < g.cols) {
+            const float gv = GradLoad<G>::load1(p.g, off + e);
+            const float mv = beta * p.m[off + e] + gv;
+            p.m[off + e] = mv;
+            y[e] = prm.nesterov ? gv + beta * mv : mv;
+          }
+        }
+      }
+    }
+    ss += y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[rr + 16 * q][cc + e] = y[e];
+    Vec4<T>::store(D + row * ldD + col, y);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int oc = rr + 16 * q;  // column of the source tile = row of the transposed output
+    f32x4_t y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = tile[cc + e][oc];
+    Vec4<T>::store(Tr + (c0 + oc) * ldT + r0 + cc, y);
+  }
+  double v[1] = {(double)ss};
+  block_sum<1>(v, red);
+  if (tid == 0) partials[blockIdx.x] = v[0];
+}
+
+template <typename T>
+__global__ __launch_bounds__(kElemThreads) void momentum_kernel(const MomTile* __restrict__ tiles,
+                                                                const MatGeom* __restrict__ geo,
+                                                                const MatPtrs* __restrict__ ptrs,
+                                                                double* __restrict__ partials,
+                                                                ElemParams prm) {
+  __shared__ float tile[kMomTile][kMomTile + 1];
+  __shared__ double red[1][4];
+  const MomTile t = tiles[blockIdx.x];
+  const MatGeom& g = geo[t.mat];
+  const MatPtrs p = ptrs[t.mat];
+  if (g.g_bf16)
+    momentum_tile<T, uint16_t>(t, g, p, partials, prm, tile, red);
+  else
+    momentum_tile<T, float>(t, g, p, partials, prm, tile, red);
+}
+
+// Sum of a matrix's block partials in block order, one wavefront per matrix:
+// lane l takes blocks l, l+64, ... then a fixed xor-shuffle tree.
+__device__ __forceinline__ double ordered_sum(const double* p, int64_t n, int64_t stride) {
+  const int lane = threadIdx.x & 63;
+  double s = 0.0;
+  for (int64_t k = lane; k < n; k += 64) s += p[k * stride];
+  return wave_sum(s);
+}
+
+__global__ __launch_bounds__(64) void finalize_norm_kernel(const MatGeom* __restrict__ geo,
+                                                           const double* __restrict__ partials,
+                                                           MatScalars* __restrict__ scal, float eps) {
+  const int mat = blockIdx.x;
+  const MatGeom& g = geo[mat];
+  const double ss = ordered_sum(partials + g.mom_tile0, g.mom_ntiles, 1);
+  if (threadIdx.x == 0) {
+    const double yn = sqrt(ss);
+    scal[mat].y_norm = yn;
+    scal[mat].s = (float)(1.0 / (yn + (double)eps));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// flat chunk kernels over W (fp32, dense) and u (compact, ns dtype).
+
+template <typename T>
+__global__ __launch_bounds__(kElemThreads) void reduce_kernel(const Chunk* __restrict__ chunks,
+                                                              const MatGeom* __restrict__ geo,
+                                                              const MatPtrs* __restrict__ ptrs,
+                                                              double* __restrict__ partials) {
+  __shared__ double red[3][4];
+  const Chunk c = chunks[blockIdx.x];
+  const MatGeom& g = geo[c.mat];
+  const float* W = ptrs[c.mat].w + c.start;
+  const T* U = reinterpret_cast<const T*>(g.U) + c.start;
+  const int tid = threadIdx.x;
+  float wu = 0.0f, uu = 0.0f, ww = 0.0f;
+  const int n4 = c.len & ~3;
+  for (int i = tid * 4; i < n4; i += kElemThreads * 4) {
+    const f32x4_t w = Vec4<float>::load(W + i);
+    const f32x4_t u = Vec4<T>::load(U + i);
+    wu += w[0] * u[0] + w[1] * u[1] + w[2] * u[2] + w[3] * u[3];
+    uu += u[0] * u[0] + u[1] * u[1] + u[2] * u[2] + u[3] * u[3];
+    ww += w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3];
+  }
+  for (int i = n4 + tid; i < c.len; i += kElemThreads) {
+    const float w = W[i];
+    float u;
+    if constexpr (sizeof(T) == 2) u = bf16_to_f32(U[i]); else u = U[i];
+    wu += w * u;
+    uu += u * u;
+    ww += w * w;
+  }
+  double v[3] = {(double)wu, (double)uu, (double)ww};
+  block_sum<3>(v, red);
+  if (tid == 0) {
+    partials[3 * (int64_t)blockIdx.x + 0] = v[0];
+    partials[3 * (int64_t)blockIdx.x + 1] = v[1];
+    partials[3 * (int64_t)blockIdx.x + 2] = v[2];
+  }
+}
+
+__global__ __launch_bounds__(64) void finalize_update_kernel(
+    const MatGeom* __restrict__ geo, const double* __restrict__ partials,
+    MatScalars* __restrict__ scal, muonh_stats* __restrict__ stats,
+    const float* __restrict__ elr_scale, ElemParams prm) {
+  const int mat = blockIdx.x;
+  const MatGeom& g = geo[mat];
+  const double* p = partials + 3 * g.chunk0;
+  const double wu = ordered_sum(p + 0, g.nchunks, 3);
+  const double uu = ordered_sum(p + 1, g.nchunks, 3);
+  const double ww = ordered_sum(p + 2, g.nchunks, 3);
+  if (threadIdx.x != 0) return;
+  const double R = scal[mat].R;
+  const double eta = (double)prm.elr * (elr_scale ? (double)elr_scale[mat] : 1.0);
+  const double un = sqrt(uu), wn = sqrt(ww);
+  double k1, k2, wt_norm, elr, inner, angle = 0.0;
+  // u^ = u / ||u||; an all-zero u gives u^ = 0 (NaN still propagates: NaN != 0).
+  inner = (un != 0.0) ? wu / un : 0.0;
+  if (prm.mode == MUONH_MODE_HYPERBALL) {
+    const double k = (un != 0.0) ? eta * R / un : 0.0;   // W~ = W - k u
+    const double wt2 = ww - 2.0 * k * wu + k * k * uu;
+    wt_norm = sqrt(wt2);
+    k1 = R / wt_norm;
+    k2 = R * k / wt_norm;
+    elr = k * un / wn;
+    const double c = inner / R;
+    const double cl = fmin(1.0, fmax(-1.0, c));
+    angle = atan2(eta * sqrt(fmax(0.0, 1.0 - cl * cl)), 1.0 - eta * cl);
+  } else if (prm.mode == MUONH_MODE_MUON_WD) {
+    k1 = 1.0 - (double)prm.weight_decay * eta;
+    k2 = eta;
+    wt_norm = sqrt(fmax(0.0, k1 * k1 * ww - 2.0 * k1 * k2 * wu + k2 * k2 * uu));
+    elr = eta * un / wn;
+  } else {
+    const double eta_t = (un != 0.0) ? eta * wn / un : 0.0;
+    k1 = 1.0;
+    k2 = eta_t;
+    wt_norm = sqrt(fmax(0.0, ww - 2.0 * k2 * wu + k2 * k2 * uu));
+    elr = eta_t * un / wn;
+  }
+  scal[mat].k1 = (float)k1;
+  scal[mat].k2 = (float)k2;
+  muonh_stats s;
+  s.y_norm = scal[mat].y_norm;
+  s.u_norm = un;
+  s.w_norm = wn;
+  s.inner = inner;
+  s.c = inner / R;
+  s.wt_norm = wt_norm;
+  s.elr = elr;
+  s.angle = angle;
+  s.nonfinite = !(isfinite(s.y_norm) && isfinite(un) && isfinite(wn) && isfinite(wt_norm) &&
+                  isfinite(inner));
+  s.reserved = 0;
+  stats[mat] = s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kElemThreads) void update_kernel(const Chunk* __restrict__ chunks,
+                                                              const MatGeom* __restrict__ geo,
+                                                              const MatPtrs* __restrict__ ptrs,
+                                                              const MatScalars* __restrict__ scal) {
+  const Chunk c = chunks[blockIdx.x];
+  const MatGeom& g = geo[c.mat];
+  float* W = ptrs[c.mat].w + c.start;
+  const T* U = reinterpret_cast<const T*>(g.U) + c.start;
+  const float k1 = scal[c.mat].k1, k2 = scal[c.mat].k2;
+  const int tid = threadIdx.x;
+  const int n4 = c.len & ~3;
+  for (int i = tid * 4; i < n4; i += kElemThreads * 4) {
+    const f32x4_t w = Vec4<float>::load(W + i);
+    const f32x4_t u = Vec4<T>::load(U + i);
+    Vec4<float>::store(W + i, k1 * w - k2 * u);
+  }
+  for (int i = n4 + tid; i < c.len; i += kElemThreads) {
+    float u;
+    if constexpr (sizeof(T) == 2) u = bf16_to_f32(U[i]); else u = U[i];
+    W[i] = k1 * W[i] - k2 * u;
+  }
+}
+
+// ||W_0||^2 partials (radius at init).
+__global__ __launch_bounds__(kElemThreads) void radius_kernel(const Chunk* __restrict__ chunks,
+                                                              const MatPtrs* __restrict__ ptrs,
+                                                              double* __restrict__ partials) {
+  __shared__ double red[1][4];
+  const Chunk c = chunks[blockIdx.x];
+  const float* W = ptrs[c.mat].w + c.start;
+  const int tid = threadIdx.x;
+  float ww = 0.0f;
+  const int n4 = c.len & ~3;
+  for (int i = tid * 4; i < n4; i += kElemThreads * 4) {
+    const f32x4_t w = Vec4<float>::load(W + i);
+    ww += w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3];
+  }
+  for (int i = n4 + tid; i < c.len; i += kElemThreads) ww += W[i] * W[i];
+  double v[1] = {(double)ww};
+  block_sum<1>(v, red);
+  if (tid == 0) partials[blockIdx.x] = v[0];
+}
+
+__global__ __launch_bounds__(64) void finalize_radius_kernel(const MatGeom* __restrict__ geo,
+                                                             const double* __restrict__ partials,
+                                                             const int32_t* __restrict__ need,
+                                                             MatScalars* __restrict__ scal) {
+  const int mat = blockIdx.x;
+  const MatGeom& g = geo[mat];
+  const double ss = ordered_sum(partials + g.chunk0, g.nchunks, 1);
+  if (threadIdx.x == 0 && need[mat]) scal[mat].R = sqrt(ss);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kElemThreads) void copy_update_kernel(const T* __restrict__ U,
+                                                                   int64_t count,
+                                                                   float* __restrict__ dst) {
+  const int64_t i = (int64_t)blockIdx.x * kElemThreads + threadIdx.x;
+  if (i >= count) return;
+  if constexpr (sizeof(T) == 2) dst[i] = bf16_to_f32(U[i]); else dst[i] = U[i];
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers
+
+hipError_t launch_momentum(int bf16, const MomTile* tiles, int64_t ntiles, const MatGeom* geo,
+                           const MatPtrs* ptrs, double* partials, ElemParams prm, hipStream_t st) {
+  if (ntiles <= 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(momentum_kernel<uint16_t>, dim3((unsigned)ntiles), dim3(kElemThreads), 0, st,
+                       tiles, geo, ptrs, partials, prm);
+  else
+    hipLaunchKernelGGL(momentum_kernel<float>, dim3((unsigned)ntiles), dim3(kElemThreads), 0, st,
+                       tiles, geo, ptrs, partials, prm);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_norm(int32_t nmat, const MatGeom* geo, const double* partials,
+                                MatScalars* scal, float eps, hipStream_t st) {
+  hipLaunchKernelGGL(finalize_norm_kernel, dim3(nmat), dim3(64), 0, st, geo, partials, scal, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(int bf16, const Chunk* chunks, int64_t nchunks, const MatGeom* geo,
+                         const MatPtrs* ptrs, double* partials, hipStream_t st) {
+  if (nchunks <= 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(reduce_kernel<uint16_t>, dim3((unsigned)nchunks), dim3(kElemThreads), 0, st,
+                       chunks, geo, ptrs, partials);
+  else
+    hipLaunchKernelGGL(reduce_kernel<float>, dim3((unsigned)nchunks), dim3(kElemThreads), 0, st,
+                       chunks, geo, ptrs, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_update(int32_t nmat, const MatGeom* geo, const double* partials,
+                                  MatScalars* scal, muonh_stats* stats, const float* elr_scale,
+                                  ElemParams prm, hipStream_t st) {
+  hipLaunchKernelGGL(finalize_update_kernel, dim3(nmat), dim3(64), 0, st, geo, partials, scal,
+                     stats, elr_scale, prm);
+  return hipGetLastError();
+}
+
+hipError_t launch_update(int bf16, const Chunk* chunks, int64_t nchunks, const MatGeom* geo,
+                         const MatPtrs* ptrs, const MatScalars* scal, hipStream_t st) {
+  if (nchunks <= 0) return hipSuccess;
+  if (bf16)
+    hipLaunchKernelGGL(update_kernel<uint16_t>, dim3((unsigned)nchunks), dim3(kElemThreads), 0, st,
+                       chunks, geo, ptrs, scal);
+  else
+    hipLaunchKernelGGL(update_kernel<float>, dim3((unsigned)nchunks), dim3(kElemThreads), 0, st,
+                       chunks, geo, ptrs, scal);
+  return hipGetLastError();
+}
+
+hipError_t launch_radius(const Chunk* chunks, int64_t nchunks, const MatPtrs* ptrs,
+                         double* partials, hipStream_t st) {
+  if (nchunks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(radius_kernel, dim3((unsigned)nchunks), dim3(kElemThreads), 0, st, chunks,
+                     ptrs, partials);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_radius(int32_t nmat, const MatGeom* geo, const double* partials,
+                                  const int32_t* need, MatScalars* scal, hipStream_t st) {
+  hipLaunchKernelGGL(finalize_radius_kernel, dim3(nmat), dim3(64), 0, st, geo, partials, need,
+                     scal);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_update(int bf16, const void* U, int64_t count, float* dst, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((count + kElemThreads - 1) / kElemThreads);
+  if (bf16)
+    hipLaunchKernelGGL(copy_update_kernel<uint16_t>, dim3(grid), dim3(kElemThreads), 0, st,
+                       reinterpret_cast<const uint16_t*>(U), count, dst);
+  else
+    hipLaunchKernelGGL(copy_update_kernel<float>, dim3(grid), dim3(kElemThreads), 0, st,
+                       reinterpret_cast<const float*>(U), count, dst);
+  return hipGetLastError();
+}
+
+}  // namespace muonh

@@ -1,0 +1,139 @@
+// Internal structures shared by the host planner (muonh.cpp) and the gfx950
+// kernels (gemm.hip, elementwise.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/muonh.h"
+
+namespace muonh {
+
+// ---------------------------------------------------------------------------
+// Tiling constants.
+
+constexpr int kGemmTile = 256;      // output tile of the grouped GEMM (M and N)
+constexpr int kGemmThreads = 256;   // 4 wavefronts of 64, 2 x 2 over the tile
+constexpr int kPad = 256;           // Newton-Schulz dims are padded to this multiple
+constexpr int kMomTile = 64;        // momentum / pack tile (64 x 64 elements)
+constexpr int kChunk = 16384;       // elements per chunk of the flat kernels
+constexpr int kElemThreads = 256;
+constexpr int kMaxXcd = 8;          // MI355X: 8 accelerator complex dies
+
+enum GemmMode : int {
+  kGram = 0,   // A = alpha * X X^T                       (alpha = s^2 on the first iteration)
+  kPoly = 1,   // B = b A + c A A
+  kApply = 2,  // X' = alpha * (a X + B X)                 (alpha = s on the first iteration)
+  kApplyLast = 3,  // kApply of the last iteration: u written compact, own orientation
+};
+
+// One problem of a grouped GEMM launch: C = P Q^T with P [M x K] and Q [N x K]
+// both row-major (K contiguous).  All dims are multiples of kGemmTile / the
+// K tile; the padding of every operand is zero.
+struct GemmProb {
+  const void* P;
+  const void* Q;
+  const void* E;   // epilogue operand read at transposed positions:
+                   //   kPoly: A (symmetric), kApply: X^T ([N x M])
+  void* O;         // row-major output [M x N] (kApply: X'), ld = ldo
+  void* OT;        // transposed output [N x M] (kApply: X'^T), ld = ldot
+  void* U;         // kApply, last iteration: compact update in the matrix's own orientation
+  int32_t M, N, K;
+  int32_t ldp, ldq, lde, ldo, ldot;
+  int32_t um, un;  // valid (unpadded) NS dims m x n of the matrix
+  int32_t u_tall;  // 1: U is [un x um] (the matrix is tall), 0: U is [um x un]
+  int32_t mat;     // matrix index
+};
+
+// Tile list entry; prob < 0 marks an empty slot (XCD balancing padding).
+struct GemmTile {
+  int32_t prob;
+  int16_t tm, tn;
+};
+
+struct MomTile {
+  int32_t mat;
+  int32_t tr, tc;  // tile coordinates in the padded, original-orientation grid
+  int32_t pad_;
+};
+
+struct Chunk {
+  int32_t mat;
+  int32_t len;
+  int64_t start;   // element offset inside the matrix
+};
+
+// Static per-matrix geometry and workspace addresses (uploaded at init).
+struct MatGeom {
+  int64_t rows, cols;
+  int32_t tall;        // rows > cols: Newton-Schulz runs on the transpose
+  int32_t g_bf16;      // gradient dtype
+  int32_t m_pad, n_pad;
+  int32_t r_pad, c_pad;  // padded dims in the matrix's own orientation
+  void* X[2];          // ping-pong iterate, [m_pad x n_pad]
+  void* XT[2];         // its transpose, [n_pad x m_pad]
+  void* U;             // compact update u, [rows x cols]
+  int64_t mom_tile0;   // first momentum tile (index into the partials array)
+  int64_t mom_ntiles;
+  int64_t chunk0;      // first flat chunk
+  int64_t nchunks;
+};
+
+// Per-step caller pointers (uploaded when they change).
+struct MatPtrs {
+  float* w;
+  const void* g;
+  float* m;
+};
+
+// Per-matrix device scalars.
+struct MatScalars {
+  double R;        // hyperball radius
+  double y_norm;   // ||Y||_F of this step
+  float s;         // 1 / (||Y|| + eps)
+  float k1, k2;    // update: W <- k1 W - k2 u
+  float pad_;
+};
+
+struct ElemParams {
+  float beta;
+  int32_t nesterov;
+  float ns_eps;
+  int32_t mode;
+  float weight_decay;
+  float elr;
+};
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (defined in the .hip files).  All return hipError_t of
+// the launch.
+
+hipError_t launch_gemm(int bf16, int mode, const GemmProb* probs, const GemmTile* tiles,
+                       int64_t ntiles, const MatScalars* scal, int first_iter, int last_iter,
+                       int symmetric, float ca, float cb, float cc, hipStream_t st);
+
+hipError_t launch_momentum(int bf16, const MomTile* tiles, int64_t ntiles, const MatGeom* geo,
+                           const MatPtrs* ptrs, double* partials, ElemParams prm, hipStream_t st);
+
+hipError_t launch_finalize_norm(int32_t nmat, const MatGeom* geo, const double* partials,
+                                MatScalars* scal, float eps, hipStream_t st);
+
+hipError_t launch_reduce(int bf16, const Chunk* chunks, int64_t nchunks, const MatGeom* geo,
+                         const MatPtrs* ptrs, double* partials, hipStream_t st);
+
+hipError_t launch_finalize_update(int32_t nmat, const MatGeom* geo, const double* partials,
+                                  MatScalars* scal, muonh_stats* stats, const float* elr_scale,
+                                  ElemParams prm, hipStream_t st);
+
+hipError_t launch_update(int bf16, const Chunk* chunks, int64_t nchunks, const MatGeom* geo,
+                         const MatPtrs* ptrs, const MatScalars* scal, hipStream_t st);
+
+hipError_t launch_radius(const Chunk* chunks, int64_t nchunks, const MatPtrs* ptrs,
+                         double* partials, hipStream_t st);
+
+hipError_t launch_finalize_radius(int32_t nmat, const MatGeom* geo, const double* partials,
+                                  const int32_t* need, MatScalars* scal, hipStream_t st);
+
+hipError_t launch_copy_update(int bf16, const void* U, int64_t count, float* dst, hipStream_t st);
+
+}  // namespace muonh

@@ -1,0 +1,803 @@
+// Host side of the MuonH library: argument validation, the plan (Newton-Schulz
+// orientation, padding, shape buckets, XCD-aware tile lists, workspace
+// layout), the launch sequence of one step and the C ABI of include/muonh.h.
+//
+// The step computed is the Hyperball update of Eq. (1) in "Puro-2B: Poor
+// Lab's Qwen2-1.5B Trained on RTX 5090 within $5090" (arXiv HTML §3.3) on
+// top of momentum and Newton-Schulz (the Muon update named there), with the
+// ordinary-Muon (Eq. (3)) and ELR-aligned (Eq. (5)) updates of §3.3.1 as
+// alternative modes.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "internal.h"
+
+using namespace muonh;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail(MUONH_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_));       \
+  } while (0)
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+constexpr int64_t kMaxDim = 1 << 16;   // padded Newton-Schulz dims fit int32 tile math
+constexpr size_t kAlign = 256;
+
+struct MatPlan {
+  int64_t rows, cols;
+  int tall, g_bf16;
+  int64_t m, n, m_pad, n_pad;
+  float radius_in;
+  size_t off_X[2], off_XT[2], off_A, off_B, off_U;
+  int64_t mom_tile0, mom_ntiles, chunk0, nchunks;
+};
+
+struct Plan {
+  muonh_options opt;
+  int32_t n = 0;
+  bool bf16 = true;
+  size_t tsize = 2;
+  std::vector<MatPlan> mats;
+  std::vector<MomTile> mom_tiles;
+  std::vector<Chunk> chunks;
+  std::vector<GemmTile> tiles[3];
+  int n_buckets = 0;
+  double ns_dense = 0, ns_exec = 0, elem_bytes = 0;
+  // workspace layout (byte offsets)
+  size_t off_geo, off_ptrs, off_scal, off_stats, off_need, off_elr;
+  size_t off_mom_tiles, off_chunks, off_tiles[3];
+  size_t off_probs_gram[2], off_probs_poly, off_probs_apply[2];
+  size_t off_part_mom, off_part_red;
+  size_t total = 0;
+};
+
+int check_options(const muonh_options& o) {
+  if (!(o.ns_steps >= 1 && o.ns_steps <= 16))
+    return fail(MUONH_EINVAL, "ns_steps must be in [1, 16]");
+  if (o.ns_dtype != MUONH_BF16 && o.ns_dtype != MUONH_F32)
+    return fail(MUONH_EINVAL, "ns_dtype must be MUONH_BF16 or MUONH_F32");
+  if (o.mode < MUONH_MODE_HYPERBALL || o.mode > MUONH_MODE_ELR_ALIGNED)
+    return fail(MUONH_EINVAL, "unknown mode");
+  if (!std::isfinite(o.beta) || !std::isfinite(o.ns_a) || !std::isfinite(o.ns_b) ||
+      !std::isfinite(o.ns_c) || !std::isfinite(o.ns_eps) || o.ns_eps < 0.0f ||
+      !std::isfinite(o.weight_decay))
+    return fail(MUONH_EINVAL, "non-finite or negative option value");
+  if (o.nesterov != 0 && o.nesterov != 1) return fail(MUONH_EINVAL, "nesterov must be 0 or 1");
+  return MUONH_OK;
+}
+
+int check_shapes(const muonh_matrix_desc* mats, int32_t n) {
+  if (n <= 0) return fail(MUONH_EINVAL, "matrix count must be >= 1");
+  if (!mats) return fail(MUONH_EINVAL, "null matrix list");
+  for (int32_t i = 0; i < n; ++i) {
+    const auto& d = mats[i];
+    if (d.rows < 1 || d.cols < 1)
+      return fail(MUONH_EINVAL, "matrix " + std::to_string(i) + ": dims must be >= 1");
+    if (std::min(d.rows, d.cols) > kMaxDim || std::max(d.rows, d.cols) > kMaxDim)
+      return fail(MUONH_EINVAL, "matrix " + std::to_string(i) + ": dims above 65536");
+    if (d.g_dtype != MUONH_F32 && d.g_dtype != MUONH_BF16)
+      return fail(MUONH_EINVAL, "matrix " + std::to_string(i) + ": g_dtype must be F32 or BF16");
+    if (!std::isfinite(d.radius))
+      return fail(MUONH_EINVAL, "matrix " + std::to_string(i) + ": non-finite radius");
+  }
+  return MUONH_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_pointers(const muonh_matrix_desc* mats, int32_t n, bool need_gm) {
+  for (int32_t i = 0; i < n; ++i) {
+    const auto& d = mats[i];
+    if (!d.w || !aligned16(d.w))
+      return fail(MUONH_EINVAL, "matrix " + std::to_string(i) + ": w is null or not 16-byte aligned");
+    if (need_gm) {
+      if (!d.g || !aligned16(d.g))
+        return fail(MUONH_EINVAL, "matrix " + std::to_string(i) + ": g is null or not 16-byte aligned");
+      if (!d.m || !aligned16(d.m))
+        return fail(MUONH_EINVAL, "matrix " + std::to_string(i) + ": m is null or not 16-byte aligned");
+    }
+  }
+  return MUONH_OK;
+}
+
+// XCD-aware tile list for one grouped GEMM launch.
+//   dims[p] = (M tiles, N tiles, K), upper = list only tm <= tn.
+// Units are (problem, group of up to 8 row panels); units are placed on the
+// 8 XCDs by longest-processing-time first, each XCD's units are ordered by
+// problem and group, tiles inside a unit run column-major (a column of 8
+// row tiles shares its Q panel, consecutive columns share the P panels), and
+// the per-XCD lists are interleaved so workgroup 8j + x runs XCD x's j-th tile.
+std::vector<GemmTile> build_tile_list(const std::vector<std::tuple<int, int, int64_t>>& dims,
+                                      bool upper) {
+  struct Unit {
+    int prob, g0, g1;
+    double cost;
+  };
+  constexpr int kGroup = 8;
+  std::vector<Unit> units;
+  for (size_t p = 0; p < dims.size(); ++p) {
+    const int mt = std::get<0>(dims[p]), nt = std::get<1>(dims[p]);
+    const int64_t K = std::get<2>(dims[p]);
+    for (int g0 = 0; g0 < mt; g0 += kGroup) {
+      const int g1 = std::min(mt, g0 + kGroup);
+      int64_t cnt = 0;
+      for (int tm = g0; tm < g1; ++tm) cnt += upper ? (nt - tm) : nt;
+      units.push_back({(int)p, g0, g1, (double)cnt * (double)K});
+    }
+  }
+  std::vector<int> order(units.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return units[a].cost > units[b].cost; });
+  std::vector<std::vector<int>> bins(kMaxXcd);
+  std::vector<double> load(kMaxXcd, 0.0);
+  for (int u : order) {
+    const int b = (int)(std::min_element(load.begin(), load.end()) - load.begin());
+    bins[b].push_back(u);
+    load[b] += units[u].cost;
+  }
+  std::vector<std::vector<GemmTile>> lists(kMaxXcd);
+  size_t longest = 0;
+  for (int x = 0; x < kMaxXcd; ++x) {
+    std::sort(bins[x].begin(), bins[x].end(), [&](int a, int b) {
+      return std::make_pair(units[a].prob, units[a].g0) < std::make_pair(units[b].prob, units[b].g0);
+    });
+    for (int u : bins[x]) {
+      const Unit& un = units[u];
+      const int nt = std::get<1>(dims[un.prob]);
+      for (int tn = 0; tn < nt; ++tn)
+        for (int tm = un.g0; tm < un.g1; ++tm)
+          if (!upper || tm <= tn) lists[x].push_back({un.prob, (int16_t)tm, (int16_t)tn});
+    }
+    longest = std::max(longest, lists[x].size());
+  }
+  std::vector<GemmTile> out(longest * kMaxXcd, GemmTile{-1, 0, 0});
+  for (int x = 0; x < kMaxXcd; ++x)
+    for (size_t j = 0; j < lists[x].size(); ++j) out[j * kMaxXcd + x] = lists[x][j];
+  // Trim trailing empty slots.
+  while (!out.empty() && out.back().prob < 0) out.pop_back();
+  return out;
+}
+
+int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& opt, Plan& P) {
+  int rc = check_options(opt);
+  if (rc) return rc;
+  rc = check_shapes(mats, n);
+  if (rc) return rc;
+  P.opt = opt;
+  P.n = n;
+  P.bf16 = opt.ns_dtype == MUONH_BF16;
+  P.tsize = P.bf16 ? 2 : 4;
+  P.mats.resize(n);
+  std::map<std::pair<int64_t, int64_t>, int> buckets;
+  int64_t mom_tiles = 0, nchunks = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    MatPlan& m = P.mats[i];
+    m.rows = mats[i].rows;
+    m.cols = mats[i].cols;
+    m.tall = m.rows > m.cols;
+    m.g_bf16 = mats[i].g_dtype == MUONH_BF16;
+    m.m = std::min(m.rows, m.cols);
+    m.n = std::max(m.rows, m.cols);
+    m.m_pad = round_up(m.m, kPad);
+    m.n_pad = round_up(m.n, kPad);
+    m.radius_in = mats[i].radius;
+    buckets[{m.m_pad, m.n_pad}]++;
+    const int64_t r_pad = m.tall ? m.n_pad : m.m_pad, c_pad = m.tall ? m.m_pad : m.n_pad;
+    m.mom_tile0 = mom_tiles;
+    m.mom_ntiles = (r_pad / kMomTile) * (c_pad / kMomTile);
+    for (int64_t tr = 0; tr < r_pad / kMomTile; ++tr)
+      for (int64_t tc = 0; tc < c_pad / kMomTile; ++tc)
+        P.mom_tiles.push_back({i, (int32_t)tr, (int32_t)tc, 0});
+    mom_tiles += m.mom_ntiles;
+    const int64_t elems = m.rows * m.cols;
+    m.chunk0 = nchunks;
+    m.nchunks = (elems + kChunk - 1) / kChunk;
+    for (int64_t s = 0; s < elems; s += kChunk)
+      P.chunks.push_back({i, (int32_t)std::min<int64_t>(kChunk, elems - s), s});
+    nchunks += m.nchunks;
+    const double mm = (double)m.m, nn = (double)m.n;
+    P.ns_dense += opt.ns_steps * (4.0 * mm * mm * nn + 2.0 * mm * mm * mm);
+    P.elem_bytes += (double)elems * ((m.g_bf16 ? 2.0 : 4.0) + 8.0 + 8.0);
+  }
+  P.n_buckets = (int)buckets.size();
+
+  // GEMM tile lists.
+  std::vector<std::tuple<int, int, int64_t>> d_gram, d_poly, d_apply;
+  for (const auto& m : P.mats) {
+    const int mt = (int)(m.m_pad / kGemmTile), nt = (int)(m.n_pad / kGemmTile);
+    d_gram.emplace_back(mt, mt, m.n_pad);
+    d_poly.emplace_back(mt, mt, m.m_pad);
+    d_apply.emplace_back(mt, nt, m.m_pad);
+  }
+  const bool sym = opt.symmetric != 0;
+  P.tiles[kGram] = build_tile_list(d_gram, sym);
+  P.tiles[kPoly] = build_tile_list(d_poly, sym);
+  P.tiles[kApply] = build_tile_list(d_apply, false);
+  for (int k = 0; k < 3; ++k)
+    for (const auto& t : P.tiles[k])
+      if (t.prob >= 0) {
+        const auto& m = P.mats[t.prob];
+        const double K = (k == kGram) ? (double)m.n_pad : (double)m.m_pad;
+        P.ns_exec += opt.ns_steps * 2.0 * kGemmTile * kGemmTile * K;
+      }
+
+  // Workspace layout: tables first, then the large per-matrix buffers.
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, kAlign);
+    return o;
+  };
+  P.off_geo = take(sizeof(MatGeom) * n);
+  P.off_ptrs = take(sizeof(MatPtrs) * n);
+  P.off_scal = take(sizeof(MatScalars) * n);
+  P.off_stats = take(sizeof(muonh_stats) * n);
+  P.off_need = take(sizeof(int32_t) * n);
+  P.off_elr = take(sizeof(float) * n);
+  P.off_mom_tiles = take(sizeof(MomTile) * P.mom_tiles.size());
+  P.off_chunks = take(sizeof(Chunk) * P.chunks.size());
+  for (int k = 0; k < 3; ++k) P.off_tiles[k] = take(sizeof(GemmTile) * std::max<size_t>(1, P.tiles[k].size()));
+  for (int k = 0; k < 2; ++k) P.off_probs_gram[k] = take(sizeof(GemmProb) * n);
+  P.off_probs_poly = take(sizeof(GemmProb) * n);
+  for (int k = 0; k < 2; ++k) P.off_probs_apply[k] = take(sizeof(GemmProb) * n);
+  P.off_part_mom = take(sizeof(double) * P.mom_tiles.size());
+  P.off_part_red = take(sizeof(double) * 3 * P.chunks.size());
+  for (auto& m : P.mats) {
+    const size_t xs = (size_t)m.m_pad * m.n_pad * P.tsize;
+    for (int k = 0; k < 2; ++k) {
+      m.off_X[k] = take(xs);
+      m.off_XT[k] = take(xs);
+    }
+    m.off_A = take((size_t)m.m_pad * m.m_pad * P.tsize);
+    m.off_B = take((size_t)m.m_pad * m.m_pad * P.tsize);
+    m.off_U = take((size_t)m.rows * m.cols * P.tsize);
+  }
+  P.total = off;
+  return MUONH_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// handle
+
+struct muonh_handle {
+  Plan plan;
+  int device = -1;
+  uint8_t* ws = nullptr;
+  bool owns_ws = false;
+  // Pinned staging for per-step uploads (pointer table, per-matrix LR factors).
+  uint8_t* staging = nullptr;
+  size_t staging_bytes = 0;
+  hipEvent_t upload_done = nullptr;
+  bool upload_pending = false;
+  std::vector<MatPtrs> cur_ptrs;   // what the device pointer table holds
+  bool ptrs_valid = false;
+  hipStream_t last_stream = nullptr;
+  int64_t steps_done = 0;
+  // timing: a ring of per-step event sets, folded into totals lazily
+  static constexpr int kRing = 4;
+  bool timing = false;
+  std::vector<hipEvent_t> ev[kRing];
+  bool ev_pending[kRing] = {false, false, false, false};
+  int ev_next = 0;
+  int ev_cur = 0;
+  double phase_total[6] = {0, 0, 0, 0, 0, 0};
+  int32_t timed_steps = 0;
+
+  template <typename T> T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
+};
+
+namespace {
+
+int upload_async(muonh_handle* h, void* dst, const void* src, size_t bytes, size_t staging_off,
+                 hipStream_t st) {
+  // The staging buffer is reused: wait until the previous upload has been
+  // consumed by the device before overwriting it.
+  if (h->upload_pending) {
+    HIP_TRY(hipEventSynchronize(h->upload_done));
+    h->upload_pending = false;
+  }
+  std::memcpy(h->staging + staging_off, src, bytes);
+  HIP_TRY(hipMemcpyAsync(dst, h->staging + staging_off, bytes, hipMemcpyHostToDevice, st));
+  return MUONH_OK;
+}
+
+int check_same_list(const muonh_handle* h, const muonh_matrix_desc* mats, int32_t n) {
+  if (n != h->plan.n) return fail(MUONH_EMISMATCH, "matrix count differs from init");
+  if (!mats) return fail(MUONH_EINVAL, "null matrix list");
+  for (int32_t i = 0; i < n; ++i) {
+    const auto& m = h->plan.mats[i];
+    if (mats[i].rows != m.rows || mats[i].cols != m.cols ||
+        (mats[i].g_dtype == MUONH_BF16) != (m.g_bf16 != 0))
+      return fail(MUONH_EMISMATCH, "matrix " + std::to_string(i) + ": shape or dtype differs from init");
+  }
+  return MUONH_OK;
+}
+
+int record(muonh_handle* h, size_t idx, hipStream_t st) {
+  if (!h->timing) return MUONH_OK;
+  HIP_TRY(hipEventRecord(h->ev[h->ev_cur][idx], st));
+  return MUONH_OK;
+}
+
+// Wait for event set k, add its phase durations to the totals.
+int fold_events(muonh_handle* h, int k) {
+  if (!h->ev_pending[k]) return MUONH_OK;
+  const auto& ev = h->ev[k];
+  const int S = h->plan.opt.ns_steps;
+  HIP_TRY(hipEventSynchronize(ev[3 * (size_t)S + 3]));
+  auto el = [&](size_t a, size_t b, double* acc) -> int {
+    float ms = 0.0f;
+    HIP_TRY(hipEventElapsedTime(&ms, ev[a], ev[b]));
+    *acc += ms;
+    return MUONH_OK;
+  };
+  int rc;
+  if ((rc = el(0, 1, &h->phase_total[0]))) return rc;
+  size_t e = 1;
+  for (int it = 0; it < S; ++it)
+    for (int k3 = 0; k3 < 3; ++k3, ++e)
+      if ((rc = el(e, e + 1, &h->phase_total[1 + k3]))) return rc;
+  if ((rc = el(e, e + 1, &h->phase_total[4]))) return rc;
+  if ((rc = el(e + 1, e + 2, &h->phase_total[5]))) return rc;
+  h->ev_pending[k] = false;
+  h->timed_steps++;
+  return MUONH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void muonh_default_options(muonh_options* opt) {
+  if (!opt) return;
+  std::memset(opt, 0, sizeof(*opt));
+  opt->beta = 0.95f;
+  opt->ns_steps = 5;
+  opt->ns_a = 3.4445f;
+  opt->ns_b = -4.7750f;
+  opt->ns_c = 2.0315f;
+  opt->ns_eps = 1e-7f;
+  opt->ns_dtype = MUONH_BF16;
+  opt->nesterov = 0;
+  opt->mode = MUONH_MODE_HYPERBALL;
+  opt->weight_decay = 0.0f;
+  opt->symmetric = 1;
+  opt->workspace = nullptr;
+  opt->workspace_bytes = 0;
+}
+
+int muonh_workspace_size(const muonh_matrix_desc* mats, int32_t n, const muonh_options* opt,
+                         size_t* bytes) {
+  if (!opt || !bytes) return fail(MUONH_EINVAL, "null argument");
+  Plan P;
+  const int rc = build_plan(mats, n, *opt, P);
+  if (rc) return rc;
+  *bytes = P.total;
+  return MUONH_OK;
+}
+
+int muonh_plan_query(const muonh_matrix_desc* mats, int32_t n, const muonh_options* opt,
+                     muonh_plan_info* info) {
+  if (!opt || !info) return fail(MUONH_EINVAL, "null argument");
+  Plan P;
+  const int rc = build_plan(mats, n, *opt, P);
+  if (rc) return rc;
+  std::memset(info, 0, sizeof(*info));
+  info->n_matrices = n;
+  info->n_buckets = P.n_buckets;
+  for (int k = 0; k < 3; ++k) {
+    int64_t c = 0;
+    for (const auto& t : P.tiles[k]) c += t.prob >= 0;
+    info->gemm_tiles[k] = c;
+  }
+  info->mom_tiles = (int64_t)P.mom_tiles.size();
+  info->flat_chunks = (int64_t)P.chunks.size();
+  info->ns_dense_flops = P.ns_dense;
+  info->ns_exec_flops = P.ns_exec;
+  info->elem_bytes = P.elem_bytes;
+  info->workspace_bytes = P.total;
+  return MUONH_OK;
+}
+
+int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
+               const muonh_options* opt, void* stream) {
+  if (!out) return fail(MUONH_EINVAL, "null handle pointer");
+  *out = nullptr;
+  if (!opt) return fail(MUONH_EINVAL, "null options");
+  Plan P;
+  int rc = build_plan(mats, n, *opt, P);
+  if (rc) return rc;
+  for (int32_t i = 0; i < n; ++i)
+    if (mats[i].radius <= 0.0f && (!mats[i].w || !aligned16(mats[i].w)))
+      return fail(MUONH_EINVAL, "matrix " + std::to_string(i) +
+                                    ": radius <= 0 needs a 16-byte aligned w to measure ||W_0||");
+  if (opt->workspace && opt->workspace_bytes < P.total)
+    return fail(MUONH_ENOMEM, "workspace too small: need " + std::to_string(P.total) + " bytes");
+  if (opt->workspace && (reinterpret_cast<uintptr_t>(opt->workspace) & (kAlign - 1)) != 0)
+    return fail(MUONH_EINVAL, "workspace must be 256-byte aligned");
+
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIP_TRY(hipGetDeviceProperties(&prop, dev));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(MUONH_ENODEV, std::string("device is ") + prop.gcnArchName + ", library is built for gfx950");
+
+  auto* h = new muonh_handle();
+  h->plan = std::move(P);
+  h->device = dev;
+  const Plan& pl = h->plan;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  auto bail = [&](int code) {
+    muonh_destroy(h);
+    return code;
+  };
+
+  h->last_stream = st;
+  if (opt->workspace) {
+    h->ws = reinterpret_cast<uint8_t*>(opt->workspace);
+  } else {
+    void* p = nullptr;
+    if (hipMalloc(&p, pl.total) != hipSuccess)
+      return bail(fail(MUONH_ENOMEM, "hipMalloc of " + std::to_string(pl.total) + " bytes failed"));
+    h->ws = reinterpret_cast<uint8_t*>(p);
+    h->owns_ws = true;
+  }
+  h->staging_bytes = align_up(sizeof(MatPtrs) * n, kAlign) + sizeof(float) * n;
+  if (hipHostMalloc(reinterpret_cast<void**>(&h->staging), h->staging_bytes, hipHostMallocDefault) !=
+      hipSuccess)
+    return bail(fail(MUONH_ENOMEM, "hipHostMalloc of the staging buffer failed"));
+  if (hipEventCreateWithFlags(&h->upload_done, hipEventDisableTiming) != hipSuccess)
+    return bail(fail(MUONH_EHIP, "hipEventCreate failed"));
+
+  // Host images of the device tables.
+  std::vector<MatGeom> geo(n);
+  std::vector<MatScalars> scal(n);
+  std::vector<int32_t> need(n);
+  std::vector<GemmProb> gram[2], poly(n), apply[2];
+  for (int k = 0; k < 2; ++k) {
+    gram[k].resize(n);
+    apply[k].resize(n);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const MatPlan& m = pl.mats[i];
+    MatGeom& g = geo[i];
+    g.rows = m.rows;
+    g.cols = m.cols;
+    g.tall = m.tall;
+    g.g_bf16 = m.g_bf16;
+    g.m_pad = (int32_t)m.m_pad;
+    g.n_pad = (int32_t)m.n_pad;
+    g.r_pad = (int32_t)(m.tall ? m.n_pad : m.m_pad);
+    g.c_pad = (int32_t)(m.tall ? m.m_pad : m.n_pad);
+    for (int k = 0; k < 2; ++k) {
+      g.X[k] = h->ws + m.off_X[k];
+      g.XT[k] = h->ws + m.off_XT[k];
+    }
+    g.U = h->ws + m.off_U;
+    g.mom_tile0 = m.mom_tile0;
+    g.mom_ntiles = m.mom_ntiles;
+    g.chunk0 = m.chunk0;
+    g.nchunks = m.nchunks;
+    scal[i] = MatScalars{m.radius_in > 0.0f ? (double)m.radius_in : 0.0, 0.0, 1.0f, 1.0f, 0.0f, 0.0f};
+    need[i] = m.radius_in > 0.0f ? 0 : 1;
+    const int32_t M = (int32_t)m.m_pad, N = (int32_t)m.n_pad;
+    for (int k = 0; k < 2; ++k) {
+      GemmProb& a = gram[k][i];
+      std::memset(&a, 0, sizeof(a));
+      a.P = a.Q = g.X[k];
+      a.O = h->ws + m.off_A;
+      a.M = a.N = M;
+      a.K = N;
+      a.ldp = a.ldq = N;
+      a.ldo = M;
+      a.mat = i;
+      GemmProb& c = apply[k][i];
+      std::memset(&c, 0, sizeof(c));
+      c.P = h->ws + m.off_B;
+      c.Q = g.XT[k];
+      c.E = g.XT[k];
+      c.O = g.X[k ^ 1];
+      c.OT = g.XT[k ^ 1];
+      c.U = g.U;
+      c.M = M;
+      c.N = N;
+      c.K = M;
+      c.ldp = M;
+      c.ldq = M;
+      c.lde = M;
+      c.ldo = N;
+      c.ldot = M;
+      c.um = (int32_t)m.m;
+      c.un = (int32_t)m.n;
+      c.u_tall = m.tall;
+      c.mat = i;
+    }
+    GemmProb& b = poly[i];
+    std::memset(&b, 0, sizeof(b));
+    b.P = b.Q = b.E = h->ws + m.off_A;
+    b.O = h->ws + m.off_B;
+    b.M = b.N = b.K = M;
+    b.ldp = b.ldq = b.lde = b.ldo = M;
+    b.mat = i;
+  }
+  auto up = [&](size_t off, const void* src, size_t bytes) -> int {
+    if (bytes) HIP_TRY(hipMemcpy(h->ws + off, src, bytes, hipMemcpyHostToDevice));
+    return MUONH_OK;
+  };
+  if ((rc = up(pl.off_geo, geo.data(), sizeof(MatGeom) * n)) ||
+      (rc = up(pl.off_scal, scal.data(), sizeof(MatScalars) * n)) ||
+      (rc = up(pl.off_need, need.data(), sizeof(int32_t) * n)) ||
+      (rc = up(pl.off_mom_tiles, pl.mom_tiles.data(), sizeof(MomTile) * pl.mom_tiles.size())) ||
+      (rc = up(pl.off_chunks, pl.chunks.data(), sizeof(Chunk) * pl.chunks.size())) ||
+      (rc = up(pl.off_probs_poly, poly.data(), sizeof(GemmProb) * n)))
+    return bail(rc);
+  for (int k = 0; k < 3; ++k)
+    if ((rc = up(pl.off_tiles[k], pl.tiles[k].data(), sizeof(GemmTile) * pl.tiles[k].size())))
+      return bail(rc);
+  for (int k = 0; k < 2; ++k)
+    if ((rc = up(pl.off_probs_gram[k], gram[k].data(), sizeof(GemmProb) * n)) ||
+        (rc = up(pl.off_probs_apply[k], apply[k].data(), sizeof(GemmProb) * n)))
+      return bail(rc);
+  // Zero the iterate / Gram buffers once so their padding starts at zero.
+  const size_t big0 = pl.mats.empty() ? pl.total : pl.mats[0].off_X[0];
+  if (hipMemsetAsync(h->ws + big0, 0, pl.total - big0, st) != hipSuccess)
+    return bail(fail(MUONH_EHIP, "hipMemsetAsync of the workspace failed"));
+
+  // Radius R = ||W_0||_F where not given.
+  bool any_need = false;
+  for (int32_t i = 0; i < n; ++i) any_need |= need[i] != 0;
+  if (any_need) {
+    std::vector<MatPtrs> ptrs(n);
+    for (int32_t i = 0; i < n; ++i)
+      ptrs[i] = MatPtrs{reinterpret_cast<float*>(mats[i].w), mats[i].g,
+                        reinterpret_cast<float*>(mats[i].m)};
+    if ((rc = up(pl.off_ptrs, ptrs.data(), sizeof(MatPtrs) * n))) return bail(rc);
+    h->cur_ptrs = ptrs;
+    h->ptrs_valid = true;
+    hipError_t e = launch_radius(h->at<Chunk>(pl.off_chunks), (int64_t)pl.chunks.size(),
+                                 h->at<MatPtrs>(pl.off_ptrs), h->at<double>(pl.off_part_red), st);
+    if (e == hipSuccess)
+      e = launch_finalize_radius(n, h->at<MatGeom>(pl.off_geo), h->at<double>(pl.off_part_red),
+                                 h->at<int32_t>(pl.off_need), h->at<MatScalars>(pl.off_scal), st);
+    if (e != hipSuccess)
+      return bail(fail(MUONH_EHIP, std::string("radius kernels: ") + hipGetErrorString(e)));
+  }
+  h->last_stream = st;
+  *out = h;
+  return MUONH_OK;
+}
+
+int muonh_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
+               const muonh_step_args* args, void* stream) {
+  if (!h || !args) return fail(MUONH_EINVAL, "null argument");
+  int rc = check_same_list(h, mats, n);
+  if (rc) return rc;
+  if ((rc = check_pointers(mats, n, true))) return rc;
+  if (!std::isfinite(args->elr)) return fail(MUONH_EINVAL, "elr is not finite");
+  const Plan& pl = h->plan;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev != h->device) return fail(MUONH_EINVAL, "current device differs from the one at init");
+
+  // Pointer table (uploaded only when the caller's pointers change).
+  std::vector<MatPtrs> ptrs(n);
+  for (int32_t i = 0; i < n; ++i)
+    ptrs[i] = MatPtrs{reinterpret_cast<float*>(mats[i].w), mats[i].g,
+                      reinterpret_cast<float*>(mats[i].m)};
+  bool uploaded = false;
+  if (!h->ptrs_valid || std::memcmp(ptrs.data(), h->cur_ptrs.data(), sizeof(MatPtrs) * n) != 0) {
+    if ((rc = upload_async(h, h->ws + pl.off_ptrs, ptrs.data(), sizeof(MatPtrs) * n, 0, st)))
+      return rc;
+    h->cur_ptrs = ptrs;
+    h->ptrs_valid = true;
+    uploaded = true;
+  }
+  const float* elr_scale_dev = nullptr;
+  if (args->elr_scale) {
+    for (int32_t i = 0; i < n; ++i)
+      if (!std::isfinite(args->elr_scale[i])) return fail(MUONH_EINVAL, "elr_scale has a non-finite entry");
+    if ((rc = upload_async(h, h->ws + pl.off_elr, args->elr_scale, sizeof(float) * n,
+                           align_up(sizeof(MatPtrs) * n, kAlign), st)))
+      return rc;
+    elr_scale_dev = h->at<float>(pl.off_elr);
+    uploaded = true;
+  }
+  if (uploaded) {
+    HIP_TRY(hipEventRecord(h->upload_done, st));
+    h->upload_pending = true;
+  }
+
+  const int S = pl.opt.ns_steps;
+  if (h->timing) {
+    const int k = h->ev_next;
+    if ((rc = fold_events(h, k))) return rc;   // the set about to be reused
+    const size_t need_ev = 2 + 3 * (size_t)S + 2;
+    while (h->ev[k].size() < need_ev) {
+      hipEvent_t e;
+      HIP_TRY(hipEventCreate(&e));
+      h->ev[k].push_back(e);
+    }
+    h->ev_cur = k;
+    h->ev_next = (k + 1) % muonh_handle::kRing;
+  }
+  const int bf = pl.bf16 ? 1 : 0;
+  ElemParams prm{pl.opt.beta, pl.opt.nesterov, pl.opt.ns_eps, pl.opt.mode, pl.opt.weight_decay,
+                 args->elr};
+  auto* geo = h->at<MatGeom>(pl.off_geo);
+  auto* dptrs = h->at<MatPtrs>(pl.off_ptrs);
+  auto* scal = h->at<MatScalars>(pl.off_scal);
+  size_t evi = 0;
+#define LAUNCH(expr)                                                                        \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess) return fail(MUONH_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+  if ((rc = record(h, evi++, st))) return rc;
+  LAUNCH(launch_momentum(bf, h->at<MomTile>(pl.off_mom_tiles), (int64_t)pl.mom_tiles.size(), geo,
+                         dptrs, h->at<double>(pl.off_part_mom), prm, st));
+  LAUNCH(launch_finalize_norm(n, geo, h->at<double>(pl.off_part_mom), scal, pl.opt.ns_eps, st));
+  if ((rc = record(h, evi++, st))) return rc;
+  for (int it = 0; it < S; ++it) {
+    const int par = it & 1;
+    const int first = it == 0, last = it == S - 1;
+    LAUNCH(launch_gemm(bf, kGram, h->at<GemmProb>(pl.off_probs_gram[par]),
+                       h->at<GemmTile>(pl.off_tiles[kGram]), (int64_t)pl.tiles[kGram].size(), scal,
+                       first, 0, pl.opt.symmetric, pl.opt.ns_a, pl.opt.ns_b, pl.opt.ns_c, st));
+    if ((rc = record(h, evi++, st))) return rc;
+    LAUNCH(launch_gemm(bf, kPoly, h->at<GemmProb>(pl.off_probs_poly),
+                       h->at<GemmTile>(pl.off_tiles[kPoly]), (int64_t)pl.tiles[kPoly].size(), scal,
+                       0, 0, pl.opt.symmetric, pl.opt.ns_a, pl.opt.ns_b, pl.opt.ns_c, st));
+    if ((rc = record(h, evi++, st))) return rc;
+    LAUNCH(launch_gemm(bf, kApply, h->at<GemmProb>(pl.off_probs_apply[par]),
+                       h->at<GemmTile>(pl.off_tiles[kApply]), (int64_t)pl.tiles[kApply].size(),
+                       scal, first, last, pl.opt.symmetric, pl.opt.ns_a, pl.opt.ns_b, pl.opt.ns_c,
+                       st));
+    if ((rc = record(h, evi++, st))) return rc;
+  }
+  LAUNCH(launch_reduce(bf, h->at<Chunk>(pl.off_chunks), (int64_t)pl.chunks.size(), geo, dptrs,
+                       h->at<double>(pl.off_part_red), st));
+  LAUNCH(launch_finalize_update(n, geo, h->at<double>(pl.off_part_red), scal,
+                                h->at<muonh_stats>(pl.off_stats), elr_scale_dev, prm, st));
+  if ((rc = record(h, evi++, st))) return rc;
+  LAUNCH(launch_update(bf, h->at<Chunk>(pl.off_chunks), (int64_t)pl.chunks.size(), geo, dptrs,
+                       scal, st));
+  if ((rc = record(h, evi++, st))) return rc;
+#undef LAUNCH
+  if (h->timing) h->ev_pending[h->ev_cur] = true;
+  h->last_stream = st;
+  h->steps_done++;
+  return MUONH_OK;
+}
+
+int muonh_get_radii(muonh_handle* h, float* out, int32_t n) {
+  if (!h || !out) return fail(MUONH_EINVAL, "null argument");
+  if (n != h->plan.n) return fail(MUONH_EMISMATCH, "count differs from init");
+  HIP_TRY(hipStreamSynchronize(h->last_stream));
+  std::vector<MatScalars> s(n);
+  HIP_TRY(hipMemcpy(s.data(), h->ws + h->plan.off_scal, sizeof(MatScalars) * n, hipMemcpyDeviceToHost));
+  for (int32_t i = 0; i < n; ++i) out[i] = (float)s[i].R;
+  return MUONH_OK;
+}
+
+int muonh_get_stats(muonh_handle* h, muonh_stats* out, int32_t n) {
+  if (!h || !out) return fail(MUONH_EINVAL, "null argument");
+  if (n != h->plan.n) return fail(MUONH_EMISMATCH, "count differs from init");
+  if (h->steps_done == 0) return fail(MUONH_ESTATE, "no step has run yet");
+  HIP_TRY(hipStreamSynchronize(h->last_stream));
+  HIP_TRY(hipMemcpy(out, h->ws + h->plan.off_stats, sizeof(muonh_stats) * n, hipMemcpyDeviceToHost));
+  return MUONH_OK;
+}
+
+int muonh_copy_update(muonh_handle* h, int32_t idx, void* dst_device, void* stream) {
+  if (!h || !dst_device) return fail(MUONH_EINVAL, "null argument");
+  if (idx < 0 || idx >= h->plan.n) return fail(MUONH_EINVAL, "matrix index out of range");
+  if (h->steps_done == 0) return fail(MUONH_ESTATE, "no step has run yet");
+  const MatPlan& m = h->plan.mats[idx];
+  const hipError_t e = launch_copy_update(h->plan.bf16 ? 1 : 0, h->ws + m.off_U, m.rows * m.cols,
+                                          reinterpret_cast<float*>(dst_device),
+                                          reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MUONH_EHIP, std::string("copy_update: ") + hipGetErrorString(e));
+  return MUONH_OK;
+}
+
+int muonh_set_timing(muonh_handle* h, int32_t enable) {
+  if (!h) return fail(MUONH_EINVAL, "null handle");
+  if (h->ws) HIP_TRY(hipStreamSynchronize(h->last_stream));
+  h->timing = enable != 0;
+  for (int k = 0; k < muonh_handle::kRing; ++k) h->ev_pending[k] = false;
+  for (double& t : h->phase_total) t = 0.0;
+  h->timed_steps = 0;
+  return MUONH_OK;
+}
+
+int muonh_get_timing(muonh_handle* h, float* phases_ms, int32_t n_phases, int32_t* n_steps) {
+  if (!h || !phases_ms || !n_steps) return fail(MUONH_EINVAL, "null argument");
+  if (n_phases < 6) return fail(MUONH_EINVAL, "need room for 6 phases");
+  // Fold the pending sets oldest first.
+  for (int j = 0; j < muonh_handle::kRing; ++j) {
+    const int k = (h->ev_next + j) % muonh_handle::kRing;
+    const int rc = fold_events(h, k);
+    if (rc) return rc;
+  }
+  for (int k = 0; k < n_phases; ++k) phases_ms[k] = k < 6 ? (float)h->phase_total[k] : 0.0f;
+  *n_steps = h->timed_steps;
+  for (double& t : h->phase_total) t = 0.0;
+  h->timed_steps = 0;
+  return MUONH_OK;
+}
+
+int muonh_destroy(muonh_handle* h) {
+  if (!h) return MUONH_OK;
+  if (h->ws) (void)hipStreamSynchronize(h->last_stream);
+  if (h->owns_ws && h->ws) (void)hipFree(h->ws);
+  if (h->staging) (void)hipHostFree(h->staging);
+  if (h->upload_done) (void)hipEventDestroy(h->upload_done);
+  for (auto& set : h->ev)
+    for (auto e : set) (void)hipEventDestroy(e);
+  delete h;
+  return MUONH_OK;
+}
+
+const char* muonh_status_str(int status) {
+  switch (status) {
+    case MUONH_OK: return "ok";
+    case MUONH_EINVAL: return "invalid argument";
+    case MUONH_EMISMATCH: return "matrix list differs from init";
+    case MUONH_ENOMEM: return "out of memory / workspace too small";
+    case MUONH_EHIP: return "HIP runtime error";
+    case MUONH_ESTATE: return "call out of order";
+    case MUONH_ENODEV: return "no usable gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+const char* muonh_last_error(void) { return g_last_error.c_str(); }
+
+double muonh_lr_linear(double eta0, double eta_min, double s, double S) {
+  if (!(S > 0.0)) return eta_min;
+  s = std::min(std::max(s, 0.0), S);
+  return eta0 + (eta_min - eta0) * s / S;
+}
+
+double muonh_lr_power(double k, double peak, double floor_, double warmup, double tau, double p) {
+  if (k <= warmup) return warmup > 0.0 ? peak * k / warmup : peak;
+  return floor_ + (peak - floor_) * std::pow(1.0 + (k - warmup) / tau, -p);
+}
+
+double muonh_lr_wsd(double k, double peak, double total, double decay_ratio, double warmup,
+                    double eta_min) {
+  if (warmup > 0.0 && k < warmup) return peak * k / warmup;
+  const double d0 = total * (1.0 - decay_ratio);
+  if (k <= d0) return peak;
+  return muonh_lr_linear(peak, eta_min, k - d0, total - d0);
+}
+
+}  // extern "C"

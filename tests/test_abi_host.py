@@ -1,0 +1,125 @@
+"""The C ABI on the host (CPU only): the library loads, exports every entry
+point the header declares, plans and validates without a device, and its
+LR helpers agree with the oracle's schedules."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import inputs
+import oracle
+import pretraining_optimizer_amd as pm
+from pretraining_optimizer_amd import muonh as mb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muonh.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muonh_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pm.load_library()
+    names = _declared_functions()
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(lib, name), name
+    bound = {n for n, _, _ in mb._SIGNATURES}
+    assert set(names) == bound
+
+
+def test_default_options():
+    o = pm.default_options()
+    assert o.beta == pytest.approx(0.95)
+    assert o.ns_steps == 5
+    assert (o.ns_a, o.ns_b, o.ns_c) == pytest.approx(oracle.NS_COEFFS_QUINTIC)
+    assert o.ns_eps == pytest.approx(1e-7)
+    assert o.ns_dtype == pm.MUONH_BF16 and o.mode == pm.MUONH_MODE_HYPERBALL and o.symmetric == 1
+
+
+def _tiles(m_pad, n_pad, sym=True):
+    mt, nt = m_pad // 256, n_pad // 256
+    gram = mt * (mt + 1) // 2 if sym else mt * mt
+    return gram, gram, mt * nt
+
+
+def test_plan_qwen3_17b_buckets_tiles_and_flops():
+    wl = inputs.workload("qwen3_1.7b")
+    info = pm.plan_query(wl.shapes)
+    assert info.n_matrices == 196 and info.n_buckets == 3
+    expect = [0, 0, 0]
+    for r, c in wl.shapes:
+        t = _tiles(min(r, c), max(r, c))
+        expect = [a + b for a, b in zip(expect, t)]
+    assert list(info.gemm_tiles) == expect
+    dense = sum(oracle.muonh.ns_dense_flops(r, c) for r, c in wl.shapes)
+    assert info.ns_dense_flops == pytest.approx(dense, rel=1e-12)
+    assert info.ns_dense_flops == pytest.approx(6.795e13, rel=1e-3)
+    assert info.mom_tiles == sum(r * c for r, c in wl.shapes) // 4096
+    assert info.elem_bytes == pytest.approx(18.0 * wl.params())
+
+
+def test_plan_pads_ragged_shapes():
+    info = pm.plan_query([(1, 1), (300, 200), (129, 4096)], pm.default_options(symmetric=0))
+    assert info.n_buckets == 3
+    # (1,1) -> 256x256; (300,200) -> 256x512 (tall: m=200, n=300); (129,4096) -> 256x4096
+    assert list(info.gemm_tiles) == [3, 3, 1 + 2 + 16]
+    assert info.flat_chunks == 1 + 4 + 33
+
+
+def test_workspace_size_matches_plan():
+    shapes = inputs.workload("diag170m").shapes
+    assert pm.workspace_size(shapes) == pm.plan_query(shapes).workspace_bytes
+    f32 = pm.workspace_size(shapes, pm.default_options(ns_dtype=pm.MUONH_F32))
+    assert f32 > pm.workspace_size(shapes)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(shapes=[(0, 5)]), dict(shapes=[(5, -1)]), dict(shapes=[(70000, 8)]),
+    dict(opts=dict(ns_steps=0)), dict(opts=dict(ns_steps=17)), dict(opts=dict(ns_dtype=7)),
+    dict(opts=dict(mode=9)), dict(opts=dict(nesterov=2)), dict(opts=dict(ns_eps=-1.0)),
+    dict(g_dtype=5),
+])
+def test_invalid_arguments_are_rejected(bad):
+    shapes = bad.get("shapes", [(8, 8)])
+    opts = pm.default_options(**bad.get("opts", {}))
+    with pytest.raises(pm.MuonHError) as ei:
+        pm.plan_query(shapes, opts, g_dtype=bad.get("g_dtype", pm.MUONH_BF16))
+    assert ei.value.status == mb.MUONH_EINVAL
+    assert pm.load_library().muonh_last_error()
+
+
+def test_null_and_empty_arguments():
+    lib = pm.load_library()
+    o = pm.default_options()
+    n = ctypes.c_size_t()
+    assert lib.muonh_workspace_size(None, 1, ctypes.byref(o), ctypes.byref(n)) == mb.MUONH_EINVAL
+    assert lib.muonh_workspace_size(mb.shape_descs([(4, 4)]), 0, ctypes.byref(o), ctypes.byref(n)) == mb.MUONH_EINVAL
+    assert lib.muonh_init(None, mb.shape_descs([(4, 4)]), 1, ctypes.byref(o), None) == mb.MUONH_EINVAL
+    h = ctypes.c_void_p()
+    # radius <= 0 with no weights to measure it from
+    assert lib.muonh_init(ctypes.byref(h), mb.shape_descs([(4, 4)], radius=0.0), 1,
+                          ctypes.byref(o), None) == mb.MUONH_EINVAL
+    assert not h.value
+    assert lib.muonh_step(None, None, 0, None, None) == mb.MUONH_EINVAL
+    assert lib.muonh_destroy(None) == mb.MUONH_OK
+    for code in (0, -1, -2, -3, -4, -5, -6, -99):
+        assert lib.muonh_status_str(code)
+
+
+def test_lr_helpers_match_oracle_schedules():
+    lib = pm.load_library()
+    for s in (0.0, 10.0, 123.4, 500.0, 900.0):
+        assert lib.muonh_lr_linear(1.04e-3, 1e-5, s, 500.0) == pytest.approx(
+            oracle.lr_linear(1.04e-3, 1e-5, s, 500.0), rel=1e-15)
+    for k in (0.0, 250.0, 1000.0, 1001.0, 69751.7, 2e5):
+        assert lib.muonh_lr_power(k, 5e-3, 5e-4, 1000.0, 1000.0, 0.5) == pytest.approx(
+            oracle.lr_phase1_power(k), rel=1e-14)
+    for k in (0, 2, 5, 7.5, 10):
+        assert lib.muonh_lr_wsd(k, 0.024, 10.0, 0.5, 0.0, 0.0) == pytest.approx(
+            oracle.lr_wsd(k, 0.024, 10, 0.5), rel=1e-14, abs=1e-18)
