@@ -25,12 +25,19 @@ __device__ __forceinline__ void st_global(void* p, V v) {
   *(MUONH_GLOBAL V*)(p) = v;
 }
 
-// fp32 -> bf16, round to nearest even (NaN stays a quiet NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);                                               // round to nearest even
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two fp32 -> packed bf16x2 (low half = a).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t h;
+  h[0] = (__bf16)a;
+  h[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
@@ -51,8 +58,8 @@ template <> struct Vec4<uint16_t> {
   }
   static __device__ __forceinline__ void store(uint16_t* p, f32x4_t v) {
     u32x2_t o;
-    o[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    o[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    o[0] = pack_bf16x2(v[0], v[1]);
+    o[1] = pack_bf16x2(v[2], v[3]);
     st_global<u32x2_t>(p, o);
   }
   static __device__ __forceinline__ void store1(uint16_t* p, float v) {

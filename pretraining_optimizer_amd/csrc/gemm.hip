@@ -15,12 +15,16 @@
 //
 // Work decomposition: a 256 x 256 output tile per workgroup of 4 wavefronts
 // (2 x 2, each 128 x 128 = 4 x 4 MFMA blocks of 32 x 32).  K advances in
-// tiles of 128 bytes per row (64 bf16 / 32 fp32), double-buffered in LDS
-// (2 stages x 2 operands x 32 KiB = 128 KiB of the 160 KiB per CU), with the
-// next tile's global loads in flight while the current one feeds the MFMAs.
-// LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by (row & 7),
-// so the 32-row MFMA operand reads and the row-wise stores are free of bank
-// conflicts without padding.
+// stages of 64 bytes per row (32 bf16 / 16 fp32) through an LDS ring filled
+// by direct-to-LDS loads
+// (global_load_lds_dwordx4: no staging registers) ring of 5 stages
+// (5 x 32 KiB = the whole 160 KiB LDS), issued three stages ahead of the MFMAs
+// that read them, with one barrier per stage placed mid-stage so the next
+// stage's first operand fragments are read while the current stage's second
+// half runs on the MFMA pipe.  LDS rows keep
+// their 16-byte chunks XOR-swizzled per row (through each lane's global
+// address), so the 32-row MFMA operand reads are free of bank conflicts
+// without padding.
 //
 // The host builds the tile list: for the symmetric products only the upper
 // tiles are listed and each off-diagonal tile also writes its mirror, and the
@@ -36,10 +40,35 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kRowBytes = 128;                       // one K tile of one row
-constexpr int kOperandBytes = kGemmTile * kRowBytes; // 32 KiB
-constexpr int kStageBytes = 2 * kOperandBytes;       // P and Q
-constexpr int kLoadsPerThread = kOperandBytes / 16 / kGemmThreads;  // 8
+constexpr int kRowBytes = 64;                        // one K stage of one row
+constexpr int kStages = 5;                           // LDS ring depth (5 x 32 KiB = 160 KiB)
+constexpr int kOperandBytes = kGemmTile * kRowBytes; // 16 KiB
+constexpr int kStageBytes = 2 * kOperandBytes;       // P and Q: 32 KiB
+constexpr int kDmaPerOperand = kOperandBytes / 1024 / 4;  // 1 KiB per wave instruction: 4
+
+#define MUONH_LDS __attribute__((address_space(3)))
+
+// Chunk c of LDS row r sits at 16-byte slot c ^ swz64(r).  For a 16-byte read
+// of one chunk by 32 consecutive rows this is free of bank conflicts whether
+// the LDS serves 8 lanes (32 banks) or 16 lanes (64 banks) per cycle.
+__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+
+// Workgroup barrier without a memory fence (the fence would drain every
+// in-flight LDS-DMA load); the empty asm statements keep the compiler from
+// moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (63 << 8));
+  asm volatile("" ::: "memory");
+}
 
 // One 16-byte LDS operand fragment x one 16-byte fragment -> 32x32 block.
 template <typename T> struct Mfma;
@@ -68,7 +97,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     const GemmProb* __restrict__ probs, const GemmTile* __restrict__ tiles,
     const MatScalars* __restrict__ scal, int first_iter, int last_iter, int symmetric,
     float ca, float cb, float cc) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
 
   const GemmTile t = tiles[blockIdx.x];
   if (t.prob < 0) return;
@@ -81,15 +110,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   const int row0 = t.tm * kGemmTile;
   const int col0 = t.tn * kGemmTile;
 
-  // Global -> LDS staging: thread owns rows (i*32 + lr), 16-byte chunk lc.
-  const int lr = tid >> 3, lc = tid & 7;
+  // Direct-to-LDS loads: one global_load_lds_dwordx4 writes 64 lanes x 16 B
+  // = 16 LDS rows of 64 B, lane L landing in row L/4, slot L%4.  Each lane
+  // therefore fetches global chunk (L%4) ^ swz64(row) of its row.  Wave w
+  // fills row blocks w, w+4, w+8, w+12 (16 rows each) of each operand.
   const size_t pstride = (size_t)pr.ldp * sizeof(T);
   const size_t qstride = (size_t)pr.ldq * sizeof(T);
-  const uint8_t* pbase = reinterpret_cast<const uint8_t*>(pr.P) + (size_t)(row0 + lr) * pstride + lc * 16;
-  const uint8_t* qbase = reinterpret_cast<const uint8_t*>(pr.Q) + (size_t)(col0 + lr) * qstride + lc * 16;
-  const int st_off = lr * kRowBytes + ((lc ^ (lr & 7)) << 4);
+  const int drow = lane >> 2;
+  const int dchunk = (lane & 3) ^ swz64(drow);
+  const uint8_t* pdma = reinterpret_cast<const uint8_t*>(pr.P) +
+                        (size_t)(row0 + wave * 16 + drow) * pstride + dchunk * 16;
+  const uint8_t* qdma = reinterpret_cast<const uint8_t*>(pr.Q) +
+                        (size_t)(col0 + wave * 16 + drow) * qstride + dchunk * 16;
+  MUONH_LDS uint8_t* lds = (MUONH_LDS uint8_t*)smem;
 
-  u32x4_t ra[kLoadsPerThread], rb[kLoadsPerThread];
   f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -98,56 +132,97 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = (int)(((size_t)pr.K * sizeof(T)) / kRowBytes);
+  const int nk = (int)(((size_t)pr.K * sizeof(T)) / kRowBytes);   // >= 8 (K >= 256)
 
-  auto gload = [&](int kt) {
+  // Enqueue K stage kt into LDS slot `slot`: 2 x kDmaPerOperand instructions
+  // per wavefront (vmcnt += 8).
+  auto issue = [&](int kt, int slot) {
+    MUONH_LDS uint8_t* st = lds + slot * kStageBytes + wave * 16 * kRowBytes;
     const size_t koff = (size_t)kt * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      ra[i] = ld_global<u32x4_t>(pbase + (size_t)(i * 32) * pstride + koff);
-      rb[i] = ld_global<u32x4_t>(qbase + (size_t)(i * 32) * qstride + koff);
+    for (int i = 0; i < kDmaPerOperand; ++i) {
+      __builtin_amdgcn_global_load_lds(
+          (const MUONH_GLOBAL void*)(pdma + (size_t)(i * 64) * pstride + koff),
+          (MUONH_LDS void*)(st + i * 64 * kRowBytes), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const MUONH_GLOBAL void*)(qdma + (size_t)(i * 64) * qstride + koff),
+          (MUONH_LDS void*)(st + kOperandBytes + i * 64 * kRowBytes), 16, 0, 0);
     }
   };
-  auto sstore = [&](int stage) {
-    uint8_t* s = smem + stage * kStageBytes + st_off;
+
+  // MFMA operand rows: 32 consecutive rows per block; (row & 15) == (lane & 15).
+  // A stage holds two 16-byte chunks per lane group: sub-steps s = 0, 1.
+  const int swz = swz64(lane & 15);
+  const int a_off = (wr * 128 + (lane & 31)) * kRowBytes;
+  const int b_off = kOperandBytes + (wc * 128 + (lane & 31)) * kRowBytes;
+  auto load_frag = [&](u32x4_t (&a)[4], u32x4_t (&b)[4], int slot, int s) {
+    const uint8_t* st = smem + slot * kStageBytes + (((s * 2 + (lane >> 5)) ^ swz) << 4);
 #pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      *reinterpret_cast<u32x4_t*>(s + i * 32 * kRowBytes) = ra[i];
-      *reinterpret_cast<u32x4_t*>(s + kOperandBytes + i * 32 * kRowBytes) = rb[i];
-    }
+    for (int i = 0; i < 4; ++i)
+      a[i] = *reinterpret_cast<const u32x4_t*>(st + a_off + i * 32 * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      b[j] = *reinterpret_cast<const u32x4_t*>(st + b_off + j * 32 * kRowBytes);
+  };
+  auto mma = [&](const u32x4_t (&a)[4], const u32x4_t (&b)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Mfma<T>::run(acc[i][j], a[i], b[j]);
+  };
+  // Wait until this wavefront's loads of the stage after the newest `ahead`
+  // issued stages have landed (vmcnt counts 2 * kDmaPerOperand per stage).
+  auto wait_stage = [&](int ahead) {
+    if (ahead >= 2) wait_vmcnt<4 * kDmaPerOperand>();
+    else if (ahead == 1) wait_vmcnt<2 * kDmaPerOperand>();
+    else wait_vmcnt<0>();
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  // MFMA operand rows: 32 consecutive rows per block; row & 7 == lane & 7.
-  const int swz = lane & 7;
-  const int a_row = wr * 128 + (lane & 31);
-  const int b_row = wc * 128 + (lane & 31);
-
+  // Pipeline (per K stage kt, LDS slot kt % 5):
+  //   A: read fragments of sub-step 1 | MFMAs of sub-step 0
+  //   B: wait for stage kt+1, barrier, refill slot (kt-1) % 5 with stage kt+4
+  //   C: read fragments of stage kt+1 sub-step 0 | MFMAs of sub-step 1
+  // The barrier in B follows every wavefront's reads of stage kt-1 (consumed
+  // by its MFMAs in the previous trip) and precedes the first read of stage
+  // kt+1.  Loads of a stage are issued three trips before it is read.
+  // Scheduling of one half-stage: the 8 fragment reads of the next sub-step
+  // are interleaved one per MFMA with the first 8 of the current 16 MFMAs,
+  // so at most 8 LDS reads are in flight (lgkmcnt stays exact) and each read
+  // has >= 8 MFMAs (>= 256 cycles) to land before it is used.
+  auto interleave = [&]() {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     // 8 MFMAs
+  };
+  u32x4_t fa0[4], fb0[4], fa1[4], fb1[4];
+  // nk >= 8: K is a multiple of 256 elements (the planner pads to it).
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  issue(3, 3);
+  wait_vmcnt<6 * kDmaPerOperand>();   // stage 0 landed, stages 1-3 in flight
+  lds_barrier();
+  load_frag(fa0, fb0, 0, 0);
+  int slot = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint8_t* sA = smem + cur * kStageBytes;
-    const uint8_t* sB = sA + kOperandBytes;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int ch = ((s * 2 + (lane >> 5)) ^ swz) << 4;
-      u32x4_t a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const u32x4_t*>(sA + (a_row + i * 32) * kRowBytes + ch);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const u32x4_t*>(sB + (b_row + j * 32) * kRowBytes + ch);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) Mfma<T>::run(acc[i][j], a[i], b[j]);
-    }
-    if (kt + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
+    const int next = (slot == kStages - 1) ? 0 : slot + 1;
+    load_frag(fa1, fb1, slot, 1);
+    mma(fa0, fb0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    // stages issued so far: up to min(kt + 3, nk - 1); wait for stage kt + 1.
+    wait_stage(min(kt + 3, nk - 1) - (kt + 1));
+    lds_barrier();
+    if (kt + 4 < nk) issue(kt + 4, (slot == 0) ? kStages - 1 : slot - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frag(fa0, fb0, next, 0);   // unused on the last trip; unconditional keeps lgkmcnt exact
+    mma(fa1, fb1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    slot = next;
   }
 
   // ---- epilogue --------------------------------------------------------
@@ -162,50 +237,156 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     alpha = (MODE == kGram) ? s * s : s;
   }
   const bool mirror = (MODE == kGram || MODE == kPoly) && symmetric && (t.tm != t.tn);
-  T* O = reinterpret_cast<T*>(MODE == kApplyLast ? pr.U : pr.O);
-  T* OT = reinterpret_cast<T*>(pr.OT);
-  const T* E = reinterpret_cast<const T*>(pr.E);
 
+  if constexpr (sizeof(T) == 2 && MODE != kApplyLast) {
+    // bf16: the wavefront's 128 x 128 sub-tile is staged through its own
+    // LDS region so that every global access is a coalesced 16-byte one: the
+    // epilogue operand E is fetched row by row (E is stored at transposed
+    // positions, so its rows are columns of the result), and each output
+    // layout is written row by row (128 rows of 256 B + 16 B pad).
+    constexpr int kEpiStride = 272;
+    lds_barrier();   // every wavefront is done reading the pipeline buffers
+    uint8_t* reg = smem + wave * 128 * kEpiStride;
+    const int wrow0 = row0 + wr * 128, wcol0 = col0 + wc * 128;
+    const int lc = lane & 31, lg = (lane >> 5) * 4;
+    if constexpr (MODE != kGram) {
+      // E sub-tile by direct-to-LDS loads into 128 rows of 256 B (no pad),
+      // 16-byte chunk q of row c at slot q ^ (c & 15).  Instruction k writes
+      // rows 4k..4k+3; lane L lands in row 4k + L/16, slot L%16.
+      const uint8_t* eb = reinterpret_cast<const uint8_t*>(pr.E) +
+                          ((size_t)wcol0 * pr.lde + wrow0) * sizeof(T);
+      const int erow = lane >> 4;
+      const int eslot = lane & 15;
+      MUONH_LDS uint8_t* ereg = (MUONH_LDS uint8_t*)reg;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+      for (int k = 0; k < 32; ++k) {
+        const int c = 4 * k + erow;
+        __builtin_amdgcn_global_load_lds(
+            (const MUONH_GLOBAL void*)(eb + (size_t)c * pr.lde * sizeof(T) + ((eslot ^ (c & 15)) << 4)),
+            (MUONH_LDS void*)(ereg + k * 1024), 16, 0, 0);
+      }
+      wait_vmcnt<0>();   // this wavefront's region only: no barrier needed
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = col0 + wc * 128 + j * 32 + (lane & 31);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int row = row0 + wr * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
-        f32x4_t v;
-        v[0] = acc[i][j][4 * g + 0];
-        v[1] = acc[i][j][4 * g + 1];
-        v[2] = acc[i][j][4 * g + 2];
-        v[3] = acc[i][j][4 * g + 3];
-        if (MODE == kGram) {
-          v *= alpha;
-        } else if (MODE == kPoly) {
-          const f32x4_t e = Vec4<T>::load(E + (size_t)col * pr.lde + row);
-          v = cb * e + cc * v;
-        } else {
-          const f32x4_t e = Vec4<T>::load(E + (size_t)col * pr.lde + row);
-          v = alpha * (ca * e + v);
-        }
-        if (MODE == kApplyLast) {
-          // u in the matrix's own orientation, compact: [um x un] or, for a
-          // tall matrix, its transpose [un x um].
-          if (col < pr.un && row < pr.um) {
-            const size_t base = pr.u_tall ? (size_t)col * pr.um + row : (size_t)row * pr.un + col;
-            const size_t step = pr.u_tall ? 1 : (size_t)pr.un;
-            Vec4<T>::store1(O + base, v[0]);
-            if (row + 1 < pr.um) Vec4<T>::store1(O + base + step, v[1]);
-            if (row + 2 < pr.um) Vec4<T>::store1(O + base + 2 * step, v[2]);
-            if (row + 3 < pr.um) Vec4<T>::store1(O + base + 3 * step, v[3]);
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4_t v;
+          v[0] = acc[i][j][4 * g + 0];
+          v[1] = acc[i][j][4 * g + 1];
+          v[2] = acc[i][j][4 * g + 2];
+          v[3] = acc[i][j][4 * g + 3];
+          if constexpr (MODE == kGram) {
+            v *= alpha;
+          } else {
+            const int ec = j * 32 + lc;
+            const u32x2_t eu = *reinterpret_cast<const u32x2_t*>(
+                reg + ec * 256 + (((i * 4 + g) ^ (ec & 15)) << 4) + lg * 2);
+            f32x4_t e;
+            e[0] = __uint_as_float(eu[0] << 16);
+            e[1] = __uint_as_float(eu[0] & 0xffff0000u);
+            e[2] = __uint_as_float(eu[1] << 16);
+            e[3] = __uint_as_float(eu[1] & 0xffff0000u);
+            if constexpr (MODE == kPoly) v = cb * e + cc * v;
+            else v = alpha * (ca * e + v);
           }
-        } else {
+          acc[i][j][4 * g + 0] = v[0];
+          acc[i][j][4 * g + 1] = v[1];
+          acc[i][j][4 * g + 2] = v[2];
+          acc[i][j][4 * g + 3] = v[3];
+        }
+    // Row-major layout.  LDS operations of one wavefront complete in issue
+    // order, so its reads below see all of its writes.
 #pragma unroll
-          for (int e = 0; e < 4; ++e) Vec4<T>::store1(O + (size_t)(row + e) * pr.ldo + col, v[e]);
-          if (MODE == kApply) {
-            Vec4<T>::store(OT + (size_t)col * pr.ldot + row, v);
-          } else if (mirror) {
-            Vec4<T>::store(O + (size_t)col * pr.ldo + row, v);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<uint16_t*>(reg + (i * 32 + g * 8 + lg + e) * kEpiStride +
+                                         (j * 32 + lc) * 2) = f32_to_bf16(acc[i][j][4 * g + e]);
+    {
+      uint8_t* ob = reinterpret_cast<uint8_t*>(pr.O) + ((size_t)wrow0 * pr.ldo + wcol0) * sizeof(T);
+#pragma unroll
+      for (int it = 0; it < 32; ++it) {
+        const int idx = it * 64 + lane, r = idx >> 4, ch = idx & 15;
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(reg + r * kEpiStride + ch * 16);
+        st_global<u32x4_t>(ob + (size_t)r * pr.ldo * sizeof(T) + ch * 16, x);
+      }
+    }
+    // Transposed layout: X'^T for kApply, the mirrored tile for the Gram products.
+    if (MODE == kApply || mirror) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            u32x2_t o;
+            o[0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+            o[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+            *reinterpret_cast<u32x2_t*>(reg + (j * 32 + lc) * kEpiStride + (i * 32 + g * 8 + lg) * 2) = o;
+          }
+      uint8_t* tb = (MODE == kApply)
+                        ? reinterpret_cast<uint8_t*>(pr.OT) + ((size_t)wcol0 * pr.ldot + wrow0) * sizeof(T)
+                        : reinterpret_cast<uint8_t*>(pr.O) + ((size_t)wcol0 * pr.ldo + wrow0) * sizeof(T);
+      const size_t tld = (size_t)((MODE == kApply) ? pr.ldot : pr.ldo) * sizeof(T);
+#pragma unroll
+      for (int it = 0; it < 32; ++it) {
+        const int idx = it * 64 + lane, c = idx >> 4, ch = idx & 15;
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(reg + c * kEpiStride + ch * 16);
+        st_global<u32x4_t>(tb + (size_t)c * tld + ch * 16, x);
+      }
+    }
+  } else {
+    T* O = reinterpret_cast<T*>(MODE == kApplyLast ? pr.U : pr.O);
+    T* OT = reinterpret_cast<T*>(pr.OT);
+    const T* E = reinterpret_cast<const T*>(pr.E);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = col0 + wc * 128 + j * 32 + (lane & 31);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int row = row0 + wr * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
+          f32x4_t v;
+          v[0] = acc[i][j][4 * g + 0];
+          v[1] = acc[i][j][4 * g + 1];
+          v[2] = acc[i][j][4 * g + 2];
+          v[3] = acc[i][j][4 * g + 3];
+          if (MODE == kGram) {
+            v *= alpha;
+          } else if (MODE == kPoly) {
+            const f32x4_t e = Vec4<T>::load(E + (size_t)col * pr.lde + row);
+            v = cb * e + cc * v;
+          } else {
+            const f32x4_t e = Vec4<T>::load(E + (size_t)col * pr.lde + row);
+            v = alpha * (ca * e + v);
+          }
+          if (MODE == kApplyLast) {
+            // u in the matrix's own orientation, compact: [um x un] or, for a
+            // tall matrix, its transpose [un x um].
+            if (col < pr.un && row < pr.um) {
+              const size_t base = pr.u_tall ? (size_t)col * pr.um + row : (size_t)row * pr.un + col;
+              const size_t step = pr.u_tall ? 1 : (size_t)pr.un;
+              Vec4<T>::store1(O + base, v[0]);
+              if (row + 1 < pr.um) Vec4<T>::store1(O + base + step, v[1]);
+              if (row + 2 < pr.um) Vec4<T>::store1(O + base + 2 * step, v[2]);
+              if (row + 3 < pr.um) Vec4<T>::store1(O + base + 3 * step, v[3]);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Vec4<T>::store1(O + (size_t)(row + e) * pr.ldo + col, v[e]);
+            if (MODE == kApply) {
+              Vec4<T>::store(OT + (size_t)col * pr.ldot + row, v);
+            } else if (mirror) {
+              Vec4<T>::store(O + (size_t)col * pr.ldo + row, v);
+            }
           }
         }
       }
