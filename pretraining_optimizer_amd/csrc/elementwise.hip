@@ -81,7 +81,7 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, const MatGeom& g
   const int64_t r0 = (int64_t)t.tr * kMomTile, c0 = (int64_t)t.tc * kMomTile;
   T* D = reinterpret_cast<T*>(g.tall ? g.XT[0] : g.X[0]);   // same orientation as M
   T* Tr = reinterpret_cast<T*>(g.tall ? g.X[0] : g.XT[0]);  // transposed
-  const int64_t ldD = g.c_pad, ldT = g.r_pad;
+  const int64_t ldD = g.c_pad + g.ld_skew, ldT = g.r_pad + g.ld_skew;
   const bool vec_ok = (g.cols & 3) == 0;
   const float beta = prm.beta;
   float ss = 0.0f;

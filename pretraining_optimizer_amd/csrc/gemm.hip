@@ -3,11 +3,12 @@
 // One launch runs one of the three products of a quintic Newton-Schulz
 // iteration for EVERY matrix of the plan, whatever its shape:
 //   kGram : A  = alpha X X^T                 (m x m, contraction over n)
-//   kPoly : B  = b A + c A A                 (m x m, contraction over m)
-//   kApply: X' = alpha (a X + B X)           (m x n, contraction over m)
+//   kPoly : B' = b A + c A A + a I           (m x m, contraction over m)
+//   kApply: X' = alpha B' X  (= alpha (a X + B X))   (m x n, contraction over m)
 // (the iteration of the Muon update; the pages name it in "Puro-2B: Poor
 // Lab's Qwen2-1.5B Trained on RTX 5090 within $5090", arXiv HTML §3.3).
 //
+// Folding a X into B' = B + a I leaves the update with no epilogue operand.
 // Every product is written as C = P Q^T with both operands row-major and the
 // contraction index contiguous, so both MFMA operands are read the same way:
 //   kGram : P = Q = X;   kPoly : P = Q = A (A is symmetric);
@@ -40,18 +41,31 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kRowBytes = 64;                        // one K stage of one row
-constexpr int kStages = 5;                           // LDS ring depth (5 x 32 KiB = 160 KiB)
-constexpr int kOperandBytes = kGemmTile * kRowBytes; // 16 KiB
-constexpr int kStageBytes = 2 * kOperandBytes;       // P and Q: 32 KiB
-constexpr int kDmaPerOperand = kOperandBytes / 1024 / 4;  // 1 KiB per wave instruction: 4
+// Operand path: register-staged loads of whole 128-byte row segments into a
+// 2-slot LDS ring (true), or direct-to-LDS loads of 64-byte row segments
+// into a 5-slot ring (false).
+constexpr bool kRegStaged = true;
+constexpr int kRowBytes = kRegStaged ? 128 : 64;     // one K stage of one row
+constexpr int kStages = kRegStaged ? 2 : 5;          // LDS ring depth
+constexpr int kOperandBytes = kGemmTile * kRowBytes; // 32 KiB / 16 KiB
+constexpr int kStageBytes = 2 * kOperandBytes;       // P and Q
+constexpr int kSubsteps = kRowBytes / 32;            // 16-deep MFMA steps per stage
+constexpr int kDmaPerOperand = 4;                    // 1 KiB per DMA instruction per wave
+// The bf16 epilogue stages each wavefront's 128 x 128 sub-tile in its own
+// region of 128 rows x (256 + 16) bytes.
+constexpr int kEpiStride = 272;
+constexpr int kEpiBytes = 4 * 128 * kEpiStride;
+constexpr int kLdsBytes = (kStages * kStageBytes > kEpiBytes) ? kStages * kStageBytes : kEpiBytes;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one CU");
 
 #define MUONH_LDS __attribute__((address_space(3)))
 
-// Chunk c of LDS row r sits at 16-byte slot c ^ swz64(r).  For a 16-byte read
+// Chunk c of LDS row r sits at 16-byte slot c ^ swz(r).  For a 16-byte read
 // of one chunk by 32 consecutive rows this is free of bank conflicts whether
 // the LDS serves 8 lanes (32 banks) or 16 lanes (64 banks) per cycle.
-__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }
+__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }    // 4 chunks/row
+__device__ __forceinline__ int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }    // 8 chunks/row
+__device__ __forceinline__ int swz_row(int r) { return kRegStaged ? swz128(r) : swz64(r); }
 
 // Workgroup barrier without a memory fence (the fence would drain every
 // in-flight LDS-DMA load); the empty asm statements keep the compiler from
@@ -97,7 +111,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     const GemmProb* __restrict__ probs, const GemmTile* __restrict__ tiles,
     const MatScalars* __restrict__ scal, int first_iter, int last_iter, int symmetric,
     float ca, float cb, float cc) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
   const GemmTile t = tiles[blockIdx.x];
   if (t.prob < 0) return;
@@ -110,18 +124,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   const int row0 = t.tm * kGemmTile;
   const int col0 = t.tn * kGemmTile;
 
-  // Direct-to-LDS loads: one global_load_lds_dwordx4 writes 64 lanes x 16 B
-  // = 16 LDS rows of 64 B, lane L landing in row L/4, slot L%4.  Each lane
-  // therefore fetches global chunk (L%4) ^ swz64(row) of its row.  Wave w
-  // fills row blocks w, w+4, w+8, w+12 (16 rows each) of each operand.
   const size_t pstride = (size_t)pr.ldp * sizeof(T);
   const size_t qstride = (size_t)pr.ldq * sizeof(T);
-  const int drow = lane >> 2;
-  const int dchunk = (lane & 3) ^ swz64(drow);
-  const uint8_t* pdma = reinterpret_cast<const uint8_t*>(pr.P) +
-                        (size_t)(row0 + wave * 16 + drow) * pstride + dchunk * 16;
-  const uint8_t* qdma = reinterpret_cast<const uint8_t*>(pr.Q) +
-                        (size_t)(col0 + wave * 16 + drow) * qstride + dchunk * 16;
   MUONH_LDS uint8_t* lds = (MUONH_LDS uint8_t*)smem;
 
   f32x16_t acc[4][4];
@@ -132,27 +136,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = (int)(((size_t)pr.K * sizeof(T)) / kRowBytes);   // >= 8 (K >= 256)
-
-  // Enqueue K stage kt into LDS slot `slot`: 2 x kDmaPerOperand instructions
-  // per wavefront (vmcnt += 8).
-  auto issue = [&](int kt, int slot) {
-    MUONH_LDS uint8_t* st = lds + slot * kStageBytes + wave * 16 * kRowBytes;
-    const size_t koff = (size_t)kt * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < kDmaPerOperand; ++i) {
-      __builtin_amdgcn_global_load_lds(
-          (const MUONH_GLOBAL void*)(pdma + (size_t)(i * 64) * pstride + koff),
-          (MUONH_LDS void*)(st + i * 64 * kRowBytes), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const MUONH_GLOBAL void*)(qdma + (size_t)(i * 64) * qstride + koff),
-          (MUONH_LDS void*)(st + kOperandBytes + i * 64 * kRowBytes), 16, 0, 0);
-    }
-  };
+  // K stages; K is a multiple of 256 elements (the planner pads to it), so
+  // nk is even and >= 4.
+  const int nk = (int)(((size_t)pr.K * sizeof(T)) / kRowBytes);
 
   // MFMA operand rows: 32 consecutive rows per block; (row & 15) == (lane & 15).
-  // A stage holds two 16-byte chunks per lane group: sub-steps s = 0, 1.
-  const int swz = swz64(lane & 15);
+  // Sub-step s reads 16-byte chunk 2s (lanes 0-31) / 2s+1 (lanes 32-63).
+  const int swz = swz_row(lane & 15);
   const int a_off = (wr * 128 + (lane & 31)) * kRowBytes;
   const int b_off = kOperandBytes + (wc * 128 + (lane & 31)) * kRowBytes;
   auto load_frag = [&](u32x4_t (&a)[4], u32x4_t (&b)[4], int slot, int s) {
@@ -170,22 +160,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) Mfma<T>::run(acc[i][j], a[i], b[j]);
   };
-  // Wait until this wavefront's loads of the stage after the newest `ahead`
-  // issued stages have landed (vmcnt counts 2 * kDmaPerOperand per stage).
-  auto wait_stage = [&](int ahead) {
-    if (ahead >= 2) wait_vmcnt<4 * kDmaPerOperand>();
-    else if (ahead == 1) wait_vmcnt<2 * kDmaPerOperand>();
-    else wait_vmcnt<0>();
-  };
-
-  // Pipeline (per K stage kt, LDS slot kt % 5):
-  //   A: read fragments of sub-step 1 | MFMAs of sub-step 0
-  //   B: wait for stage kt+1, barrier, refill slot (kt-1) % 5 with stage kt+4
-  //   C: read fragments of stage kt+1 sub-step 0 | MFMAs of sub-step 1
-  // The barrier in B follows every wavefront's reads of stage kt-1 (consumed
-  // by its MFMAs in the previous trip) and precedes the first read of stage
-  // kt+1.  Loads of a stage are issued three trips before it is read.
-  // Scheduling of one half-stage: the 8 fragment reads of the next sub-step
+  // Scheduling of one sub-step: the 8 fragment reads of the next sub-step
   // are interleaved one per MFMA with the first 8 of the current 16 MFMAs,
   // so at most 8 LDS reads are in flight (lgkmcnt stays exact) and each read
   // has >= 8 MFMAs (>= 256 cycles) to land before it is used.
@@ -198,32 +173,162 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     // 8 MFMAs
   };
   u32x4_t fa0[4], fb0[4], fa1[4], fb1[4];
-  // nk >= 8: K is a multiple of 256 elements (the planner pads to it).
-  issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
-  issue(3, 3);
-  wait_vmcnt<6 * kDmaPerOperand>();   // stage 0 landed, stages 1-3 in flight
-  lds_barrier();
-  load_frag(fa0, fb0, 0, 0);
-  int slot = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int next = (slot == kStages - 1) ? 0 : slot + 1;
-    load_frag(fa1, fb1, slot, 1);
-    mma(fa0, fb0);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    // stages issued so far: up to min(kt + 3, nk - 1); wait for stage kt + 1.
-    wait_stage(min(kt + 3, nk - 1) - (kt + 1));
+
+  if constexpr (kRegStaged) {
+    // Thread t owns rows (i*32 + t/8) and 16-byte chunk t%8 of each operand,
+    // so one load instruction of a wavefront covers 8 whole 128-byte lines.
+    // Stage s is loaded into one of two register sets during stage s-3 (P
+    // half in sub-step 1, Q half in sub-step 2), written to LDS slot s%2
+    // during stage s-1 (P in sub-step 0, Q in sub-step 1) and published by
+    // the barrier that stage s-1 places before its last sub-step.  Loads and
+    // LDS writes are spread one per MFMA or two so the in-order issue never
+    // stalls the MFMA pipe behind a full memory queue.
+    static_assert(kSubsteps == 4, "the stage schedule below assumes 4 sub-steps");
+    constexpr int kLd = kOperandBytes / 16 / kGemmThreads;   // 8 loads per operand
+    const int srow = tid >> 3, schunk = tid & 7;
+    const uint8_t* pg = reinterpret_cast<const uint8_t*>(pr.P) + (size_t)(row0 + srow) * pstride + schunk * 16;
+    const uint8_t* qg = reinterpret_cast<const uint8_t*>(pr.Q) + (size_t)(col0 + srow) * qstride + schunk * 16;
+    const int sst = srow * kRowBytes + ((schunk ^ swz128(srow & 15)) << 4);
+    u32x4_t ra0[kLd], rb0[kLd], ra1[kLd], rb1[kLd];
+    auto gload_half = [&](u32x4_t (&r)[kLd], const uint8_t* g, size_t stride, int kt) {
+      const size_t koff = (size_t)min(kt, nk - 1) * kRowBytes;   // tail: reload the last stage
+#pragma unroll
+      for (int i = 0; i < kLd; ++i) r[i] = ld_global<u32x4_t>(g + (size_t)(i * 32) * stride + koff);
+    };
+    auto sstore_half = [&](const u32x4_t (&r)[kLd], int slot, int operand) {
+      uint8_t* st = smem + slot * kStageBytes + operand * kOperandBytes + sst;
+#pragma unroll
+      for (int i = 0; i < kLd; ++i) *reinterpret_cast<u32x4_t*>(st + i * 32 * kRowBytes) = r[i];
+    };
+    // s_waitcnt lgkmcnt(0) alone: this wavefront's LDS accesses are done.
+    auto wait_lds = [&]() {
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+      asm volatile("" ::: "memory");
+    };
+    // One K stage read from LDS slot `cur`; register set (ra, rb) holds the
+    // next stage, which goes to slot `nxt`, and is then refilled with stage
+    // kt_load.  On entry fa0/fb0 hold sub-step 0 of this stage; on exit they
+    // hold sub-step 0 of the next stage.
+    auto stage = [&](u32x4_t (&ra)[kLd], u32x4_t (&rb)[kLd], int cur, int nxt, int kt_load) {
+      // sub-step 0: MFMA, frag read, MFMA, LDS write (P half of the next stage)
+      load_frag(fa1, fb1, cur, 1);
+      mma(fa0, fb0);
+      sstore_half(ra, nxt, 0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // sub-step 1: + LDS writes of the Q half, refill of the P half
+      load_frag(fa0, fb0, cur, 2);
+      mma(fa1, fb1);
+      sstore_half(rb, nxt, 1);
+      gload_half(ra, pg, pstride, kt_load);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // sub-step 2: + refill of the Q half
+      load_frag(fa1, fb1, cur, 3);
+      mma(fa0, fb0);
+      gload_half(rb, qg, qstride, kt_load);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // the next stage is in LDS; every wavefront has its last fragments of
+      // this stage in registers, so slot `cur` may be rewritten after this
+      wait_lds();
+      lds_barrier();
+      // sub-step 3: + fragments of the next stage's sub-step 0
+      load_frag(fa0, fb0, nxt, 0);
+      mma(fa1, fb1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    gload_half(ra0, pg, pstride, 0);
+    gload_half(rb0, qg, qstride, 0);
+    gload_half(ra1, pg, pstride, 1);
+    gload_half(rb1, qg, qstride, 1);
+    sstore_half(ra0, 0, 0);    // stage 0 -> slot 0
+    sstore_half(rb0, 0, 1);
+    gload_half(ra0, pg, pstride, 2);
+    gload_half(rb0, qg, qstride, 2);
+    wait_lds();
     lds_barrier();
-    if (kt + 4 < nk) issue(kt + 4, (slot == 0) ? kStages - 1 : slot - 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frag(fa0, fb0, next, 0);   // unused on the last trip; unconditional keeps lgkmcnt exact
-    mma(fa1, fb1);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    slot = next;
+    load_frag(fa0, fb0, 0, 0);
+    // nk is even: two stages per trip, register sets alternating.
+    for (int kt = 0; kt < nk; kt += 2) {
+      stage(ra1, rb1, 0, 1, kt + 3);   // stage kt   (slot 0); set 1 = stage kt+1
+      stage(ra0, rb0, 1, 0, kt + 4);   // stage kt+1 (slot 1); set 0 = stage kt+2
+    }
+  } else {
+    // Direct-to-LDS loads: one global_load_lds_dwordx4 writes 64 lanes x 16 B
+    // = 16 LDS rows of 64 B, lane L landing in row L/4, slot L%4.  Each lane
+    // therefore fetches global chunk (L%4) ^ swz64(row) of its row.  Wave w
+    // fills row blocks w, w+4, w+8, w+12 (16 rows each) of each operand.
+    const int drow = lane >> 2;
+    const int dchunk = (lane & 3) ^ swz64(drow);
+    const uint8_t* pdma = reinterpret_cast<const uint8_t*>(pr.P) +
+                          (size_t)(row0 + wave * 16 + drow) * pstride + dchunk * 16;
+    const uint8_t* qdma = reinterpret_cast<const uint8_t*>(pr.Q) +
+                          (size_t)(col0 + wave * 16 + drow) * qstride + dchunk * 16;
+    auto issue = [&](int kt, int slot) {
+      MUONH_LDS uint8_t* st = lds + slot * kStageBytes + wave * 16 * kRowBytes;
+      const size_t koff = (size_t)kt * kRowBytes;
+#pragma unroll
+      for (int i = 0; i < kDmaPerOperand; ++i) {
+        __builtin_amdgcn_global_load_lds(
+            (const MUONH_GLOBAL void*)(pdma + (size_t)(i * 64) * pstride + koff),
+            (MUONH_LDS void*)(st + i * 64 * kRowBytes), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const MUONH_GLOBAL void*)(qdma + (size_t)(i * 64) * qstride + koff),
+            (MUONH_LDS void*)(st + kOperandBytes + i * 64 * kRowBytes), 16, 0, 0);
+      }
+    };
+    auto wait_stage = [&](int ahead) {
+      if (ahead >= 2) wait_vmcnt<4 * kDmaPerOperand>();
+      else if (ahead == 1) wait_vmcnt<2 * kDmaPerOperand>();
+      else wait_vmcnt<0>();
+    };
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    issue(3, 3);
+    wait_vmcnt<6 * kDmaPerOperand>();   // stage 0 landed, stages 1-3 in flight
+    lds_barrier();
+    load_frag(fa0, fb0, 0, 0);
+    int slot = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int next = (slot == kStages - 1) ? 0 : slot + 1;
+      load_frag(fa1, fb1, slot, 1);
+      mma(fa0, fb0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      wait_stage(min(kt + 3, nk - 1) - (kt + 1));
+      lds_barrier();
+      if (kt + 4 < nk) issue(kt + 4, (slot == 0) ? kStages - 1 : slot - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_frag(fa0, fb0, next, 0);
+      mma(fa1, fb1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      slot = next;
+    }
   }
+  wait_vmcnt<0>();   // no load in flight into LDS or registers past this point
 
   // ---- epilogue --------------------------------------------------------
   // Accumulator register r of block (i, j) holds C[row][col] with
@@ -244,12 +349,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     // epilogue operand E is fetched row by row (E is stored at transposed
     // positions, so its rows are columns of the result), and each output
     // layout is written row by row (128 rows of 256 B + 16 B pad).
-    constexpr int kEpiStride = 272;
     lds_barrier();   // every wavefront is done reading the pipeline buffers
     uint8_t* reg = smem + wave * 128 * kEpiStride;
     const int wrow0 = row0 + wr * 128, wcol0 = col0 + wc * 128;
     const int lc = lane & 31, lg = (lane >> 5) * 4;
-    if constexpr (MODE != kGram) {
+    if constexpr (MODE == kPoly) {
       // E sub-tile by direct-to-LDS loads into 128 rows of 256 B (no pad),
       // 16-byte chunk q of row c at slot q ^ (c & 15).  Instruction k writes
       // rows 4k..4k+3; lane L lands in row 4k + L/16, slot L%16.
@@ -278,9 +382,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
           v[1] = acc[i][j][4 * g + 1];
           v[2] = acc[i][j][4 * g + 2];
           v[3] = acc[i][j][4 * g + 3];
-          if constexpr (MODE == kGram) {
-            v *= alpha;
-          } else {
+          if constexpr (MODE == kPoly) {
             const int ec = j * 32 + lc;
             const u32x2_t eu = *reinterpret_cast<const u32x2_t*>(
                 reg + ec * 256 + (((i * 4 + g) ^ (ec & 15)) << 4) + lg * 2);
@@ -289,8 +391,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
             e[1] = __uint_as_float(eu[0] & 0xffff0000u);
             e[2] = __uint_as_float(eu[1] << 16);
             e[3] = __uint_as_float(eu[1] & 0xffff0000u);
-            if constexpr (MODE == kPoly) v = cb * e + cc * v;
-            else v = alpha * (ca * e + v);
+            v = cb * e + cc * v;
+            // + a on the (valid) diagonal
+            const int grow = wrow0 + i * 32 + g * 8 + lg, gcol = wcol0 + j * 32 + lc;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (grow + q == gcol && gcol < pr.um) v[q] += ca;
+          } else {
+            v *= alpha;
           }
           acc[i][j][4 * g + 0] = v[0];
           acc[i][j][4 * g + 1] = v[1];
@@ -359,14 +467,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
           v[1] = acc[i][j][4 * g + 1];
           v[2] = acc[i][j][4 * g + 2];
           v[3] = acc[i][j][4 * g + 3];
-          if (MODE == kGram) {
-            v *= alpha;
-          } else if (MODE == kPoly) {
+          if (MODE == kPoly) {
             const f32x4_t e = Vec4<T>::load(E + (size_t)col * pr.lde + row);
             v = cb * e + cc * v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (row + q == col && col < pr.um) v[q] += ca;   // + a I
           } else {
-            const f32x4_t e = Vec4<T>::load(E + (size_t)col * pr.lde + row);
-            v = alpha * (ca * e + v);
+            v *= alpha;
           }
           if (MODE == kApplyLast) {
             // u in the matrix's own orientation, compact: [um x un] or, for a

@@ -15,6 +15,7 @@ namespace muonh {
 constexpr int kGemmTile = 256;      // output tile of the grouped GEMM (M and N)
 constexpr int kGemmThreads = 256;   // 4 wavefronts of 64, 2 x 2 over the tile
 constexpr int kPad = 256;           // Newton-Schulz dims are padded to this multiple
+constexpr int kRowSkewBytes = 128;  // extra bytes per row of every Newton-Schulz buffer
 constexpr int kMomTile = 64;        // momentum / pack tile (64 x 64 elements)
 constexpr int kChunk = 16384;       // elements per chunk of the flat kernels
 constexpr int kElemThreads = 256;
@@ -22,8 +23,8 @@ constexpr int kMaxXcd = 8;          // MI355X: 8 accelerator complex dies
 
 enum GemmMode : int {
   kGram = 0,   // A = alpha * X X^T                       (alpha = s^2 on the first iteration)
-  kPoly = 1,   // B = b A + c A A
-  kApply = 2,  // X' = alpha * (a X + B X)                 (alpha = s on the first iteration)
+  kPoly = 1,   // B' = b A + c A A + a I
+  kApply = 2,  // X' = alpha * B' X = alpha * (a X + B X)   (alpha = s on the first iteration)
   kApplyLast = 3,  // kApply of the last iteration: u written compact, own orientation
 };
 
@@ -33,14 +34,13 @@ enum GemmMode : int {
 struct GemmProb {
   const void* P;
   const void* Q;
-  const void* E;   // epilogue operand read at transposed positions:
-                   //   kPoly: A (symmetric), kApply: X^T ([N x M])
+  const void* E;   // epilogue operand read at transposed positions: kPoly: A (symmetric)
   void* O;         // row-major output [M x N] (kApply: X'), ld = ldo
   void* OT;        // transposed output [N x M] (kApply: X'^T), ld = ldot
   void* U;         // kApply, last iteration: compact update in the matrix's own orientation
   int32_t M, N, K;
   int32_t ldp, ldq, lde, ldo, ldot;
-  int32_t um, un;  // valid (unpadded) NS dims m x n of the matrix
+  int32_t um, un;  // valid (unpadded) NS dims m x n of the matrix (kPoly: um for the diagonal)
   int32_t u_tall;  // 1: U is [un x um] (the matrix is tall), 0: U is [um x un]
   int32_t mat;     // matrix index
 };
@@ -70,6 +70,7 @@ struct MatGeom {
   int32_t g_bf16;      // gradient dtype
   int32_t m_pad, n_pad;
   int32_t r_pad, c_pad;  // padded dims in the matrix's own orientation
+  int32_t ld_skew;     // elements added to every row pitch (kRowSkewBytes / element size)
   void* X[2];          // ping-pong iterate, [m_pad x n_pad]
   void* XT[2];         // its transpose, [n_pad x m_pad]
   void* U;             // compact update u, [rows x cols]

@@ -265,14 +265,18 @@ int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& op
   for (int k = 0; k < 2; ++k) P.off_probs_apply[k] = take(sizeof(GemmProb) * n);
   P.off_part_mom = take(sizeof(double) * P.mom_tiles.size());
   P.off_part_red = take(sizeof(double) * 3 * P.chunks.size());
+  // Every Newton-Schulz buffer row is kRowSkewBytes longer than the padded
+  // dim: with power-of-two pitches the 256 rows a tile streams at one K
+  // offset would all land in the same L2 channel.
+  const int64_t skew = kRowSkewBytes / (int64_t)P.tsize;
   for (auto& m : P.mats) {
-    const size_t xs = (size_t)m.m_pad * m.n_pad * P.tsize;
+    const size_t ldn = (size_t)(m.n_pad + skew), ldm = (size_t)(m.m_pad + skew);
     for (int k = 0; k < 2; ++k) {
-      m.off_X[k] = take(xs);
-      m.off_XT[k] = take(xs);
+      m.off_X[k] = take((size_t)m.m_pad * ldn * P.tsize);
+      m.off_XT[k] = take((size_t)m.n_pad * ldm * P.tsize);
     }
-    m.off_A = take((size_t)m.m_pad * m.m_pad * P.tsize);
-    m.off_B = take((size_t)m.m_pad * m.m_pad * P.tsize);
+    m.off_A = take((size_t)m.m_pad * ldm * P.tsize);
+    m.off_B = take((size_t)m.m_pad * ldm * P.tsize);
     m.off_U = take((size_t)m.rows * m.cols * P.tsize);
   }
   P.total = off;
@@ -495,6 +499,7 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
     g.n_pad = (int32_t)m.n_pad;
     g.r_pad = (int32_t)(m.tall ? m.n_pad : m.m_pad);
     g.c_pad = (int32_t)(m.tall ? m.m_pad : m.n_pad);
+    g.ld_skew = (int32_t)(kRowSkewBytes / pl.tsize);
     for (int k = 0; k < 2; ++k) {
       g.X[k] = h->ws + m.off_X[k];
       g.XT[k] = h->ws + m.off_XT[k];
@@ -507,6 +512,7 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
     scal[i] = MatScalars{m.radius_in > 0.0f ? (double)m.radius_in : 0.0, 0.0, 1.0f, 1.0f, 0.0f, 0.0f};
     need[i] = m.radius_in > 0.0f ? 0 : 1;
     const int32_t M = (int32_t)m.m_pad, N = (int32_t)m.n_pad;
+    const int32_t LM = M + g.ld_skew, LN = N + g.ld_skew;   // row pitches
     for (int k = 0; k < 2; ++k) {
       GemmProb& a = gram[k][i];
       std::memset(&a, 0, sizeof(a));
@@ -514,25 +520,25 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
       a.O = h->ws + m.off_A;
       a.M = a.N = M;
       a.K = N;
-      a.ldp = a.ldq = N;
-      a.ldo = M;
+      a.ldp = a.ldq = LN;
+      a.ldo = LM;
       a.mat = i;
       GemmProb& c = apply[k][i];
       std::memset(&c, 0, sizeof(c));
       c.P = h->ws + m.off_B;
       c.Q = g.XT[k];
-      c.E = g.XT[k];
+      c.E = nullptr;
       c.O = g.X[k ^ 1];
       c.OT = g.XT[k ^ 1];
       c.U = g.U;
       c.M = M;
       c.N = N;
       c.K = M;
-      c.ldp = M;
-      c.ldq = M;
-      c.lde = M;
-      c.ldo = N;
-      c.ldot = M;
+      c.ldp = LM;
+      c.ldq = LM;
+      c.lde = LM;
+      c.ldo = LN;
+      c.ldot = LM;
       c.um = (int32_t)m.m;
       c.un = (int32_t)m.n;
       c.u_tall = m.tall;
@@ -543,7 +549,8 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
     b.P = b.Q = b.E = h->ws + m.off_A;
     b.O = h->ws + m.off_B;
     b.M = b.N = b.K = M;
-    b.ldp = b.ldq = b.lde = b.ldo = M;
+    b.ldp = b.ldq = b.lde = b.ldo = LM;
+    b.um = (int32_t)m.m;
     b.mat = i;
   }
   auto up = [&](size_t off, const void* src, size_t bytes) -> int {
