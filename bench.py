@@ -64,6 +64,38 @@ def per_kernel_work(shapes, ns_steps, tsize, gsize):
     return f, b, params
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_apply_qwen3_1.7b_traffic.md")
+KERNEL_SOURCES = ("gemm.hip", "device_util.h", "internal.h")
+
+
+def kernel_source_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "pretraining_optimizer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    profile (FETCH_SIZE and WRITE_SIZE runs, calibrated against a plain copy),
+    or None when there is none or the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    kv = {}
+    for line in lines:
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            kv[k.strip()] = v.strip().strip("`")
+    if kv.get("kernel-source-sha256") != kernel_source_sha() or kv.get("kernel") != kernel:
+        return None
+    return float(kv["hbm-bytes-per-launch"])
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -108,6 +140,8 @@ def main():
     ap.add_argument("--cpu-mats", type=int, default=7,
                     help="matrices the CPU oracle times (default: one layer)")
     ap.add_argument("--grad-sets", type=int, default=4)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="also run one plain device-to-device copy of BYTES (for counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -138,6 +172,16 @@ def main():
     if not args.no_cpu_baseline:
         # keep the step-0 inputs of the sampled matrices for the oracle
         cpu_inputs = ([w.clone() for w in ws[:args.cpu_mats]], pool[0][:args.cpu_mats])
+
+    if args.copy_calibration > 0:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {4 * n} bytes done")
+        del src, dst
 
     opt = pm.MuonH(ws, ms, grad_dtype=wl.g_dtype,
                    ns_dtype=pm.MUONH_BF16 if ns == "bf16" else pm.MUONH_F32)
@@ -173,31 +217,41 @@ def main():
     flops, bytes_, params = per_kernel_work(wl.shapes, S, tsize, gsize)
     per_step = {k: v / nt for k, v in phases.items()}
     peak = PEAK_BF16_TFLOPS if ns == "bf16" else PEAK_F32_TFLOPS
+    # launches per step of each NS kernel and its share of the dense FLOP
+    launches = {"ns_gram": S, "ns_poly": S, "ns_apply": S - 1, "ns_apply_last": 1}
+    fl = {"ns_gram": flops["ns_gram"], "ns_poly": flops["ns_poly"],
+          "ns_apply": flops["ns_apply"] * (S - 1) / S, "ns_apply_last": flops["ns_apply"] / S}
     kern = {}
-    for k in ("ns_gram", "ns_poly", "ns_apply"):
-        t_launch = per_step[k] / S
-        tf = flops[k] / S / (t_launch * 1e-3) / 1e12
-        kern[k] = {"ms_per_launch": t_launch, "dense_tflops": tf, "frac_of_peak": tf / peak}
+    for k in ("ns_gram", "ns_poly", "ns_apply", "ns_apply_last"):
+        if launches[k] == 0:
+            continue
+        t_launch = per_step[k] / launches[k]
+        tf = fl[k] / launches[k] / (t_launch * 1e-3) / 1e12
+        kern[k] = {"ms_per_launch": t_launch, "launches_per_step": launches[k],
+                   "dense_tflops": tf, "frac_of_peak": tf / peak}
     for k in ("momentum", "reduce", "update"):
         gbs = bytes_[k] / (per_step[k] * 1e-3) / 1e9
         kern[k] = {"ms": per_step[k], "gbs": gbs, "frac_of_hbm": gbs / PEAK_HBM_GBS}
-    ns_ms = sum(per_step[k] for k in ("ns_gram", "ns_poly", "ns_apply"))
+    ns_ms = sum(per_step[k] for k in ("ns_gram", "ns_poly", "ns_apply", "ns_apply_last"))
     el_ms = sum(per_step[k] for k in ("momentum", "reduce", "update"))
     ns_tflops = info.ns_dense_flops / (ns_ms * 1e-3) / 1e12
     el_gbs = sum(bytes_.values()) / (el_ms * 1e-3) / 1e9
     alg_gbs = info.elem_bytes / (el_ms * 1e-3) / 1e9
     for k, v in per_step.items():
-        log(f"  {k:9s} {v:8.3f} ms/step  {kern[k]}")
+        log(f"  {k:13s} {v:8.3f} ms/step  {kern.get(k)}")
     log(f"  NS total {ns_ms:.3f} ms: {ns_tflops:.1f} dense TFLOP/s ({ns_tflops / peak:.1%} of peak); "
         f"elementwise {el_ms:.3f} ms: {el_gbs:.0f} GB/s kernel bytes, {alg_gbs:.0f} GB/s at 18 B/param")
 
-    dom = max(("ns_gram", "ns_poly", "ns_apply"), key=lambda k: per_step[k])
+    # The dominant kernel: the NS product with the largest share of the step.
+    names = {"ns_gram": "gemm_kernel<bf16, kGram> (A = X X^T)",
+             "ns_poly": "gemm_kernel<bf16, kPoly> (B' = b A + c A A + a I)",
+             "ns_apply": "gemm_kernel<bf16, kApply> (X' = B' X)",
+             "ns_apply_last": "gemm_kernel<bf16, kApplyLast> (u = B' X)"}
+    dom = max((k for k in kern if k in names), key=lambda k: per_step[k])
     roof = {"bound": "mfma", "achieved": kern[dom]["dense_tflops"], "peak": peak, "unit": "TFLOP/s",
-            "frac": kern[dom]["dense_tflops"] / peak, "traffic": None,
-            "kernel": {"ns_gram": "gemm_kernel<bf16, kGram> (X X^T)",
-                       "ns_poly": "gemm_kernel<bf16, kPoly> (b A + c A A)",
-                       "ns_apply": "gemm_kernel<bf16, kApply> (a X + B X)"}[dom],
-            "flop_per_launch": flops[dom] / S, "ms_per_launch": kern[dom]["ms_per_launch"]}
+            "frac": kern[dom]["dense_tflops"] / peak, "traffic": traffic_for(dom),
+            "kernel": names[dom], "flop_per_launch": fl[dom] / launches[dom],
+            "ms_per_launch": kern[dom]["ms_per_launch"]}
 
     cpu = None
     if cpu_inputs is not None:

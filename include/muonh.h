@@ -161,9 +161,11 @@ int muonh_copy_update(muonh_handle* h, int32_t idx, void* dst_device, void* stre
  * muonh_set_timing(h, 1) starts recording (and clears the totals); every
  * later step records one event after each launch.  muonh_get_timing
  * synchronises, writes the totals in milliseconds over the *n_steps timed
- * steps since the last read into phases_ms[0..5] = momentum+pack (and its
- * finalise), NS X X^T, NS A A, NS B X (each summed over the ns_steps
- * launches), reductions (+finalise), update; then clears the totals.        */
+ * steps since the last read into phases_ms[0..6] = momentum+pack (and its
+ * finalise), NS X X^T, NS A A (each summed over the ns_steps launches), NS
+ * B X (summed over the first ns_steps-1 launches), the last NS B X launch
+ * (it writes u), reductions (+finalise), update; then clears the totals.
+ * n_phases must be >= 7.                                                    */
 int muonh_set_timing(muonh_handle* h, int32_t enable);
 int muonh_get_timing(muonh_handle* h, float* phases_ms, int32_t n_phases, int32_t* n_steps);
 

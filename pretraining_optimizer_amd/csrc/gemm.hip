@@ -343,7 +343,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   }
   const bool mirror = (MODE == kGram || MODE == kPoly) && symmetric && (t.tm != t.tn);
 
-  if constexpr (sizeof(T) == 2 && MODE != kApplyLast) {
+  if constexpr (sizeof(T) == 2) {
     // bf16: the wavefront's 128 x 128 sub-tile is staged through its own
     // LDS region so that every global access is a coalesced 16-byte one: the
     // epilogue operand E is fetched row by row (E is stored at transposed
@@ -405,29 +405,23 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
           acc[i][j][4 * g + 2] = v[2];
           acc[i][j][4 * g + 3] = v[3];
         }
-    // Row-major layout.  LDS operations of one wavefront complete in issue
-    // order, so its reads below see all of its writes.
+    // The sub-tile goes to LDS row-major (2-byte writes, 4 per register group)
+    // or transposed (one 8-byte write per register group), then leaves as
+    // rows of 256 B.  LDS operations of one wavefront complete in issue
+    // order, so its reads see all of its writes.
+    auto lds_rowmajor = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+          for (int g = 0; g < 4; ++g)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<uint16_t*>(reg + (i * 32 + g * 8 + lg + e) * kEpiStride +
-                                         (j * 32 + lc) * 2) = f32_to_bf16(acc[i][j][4 * g + e]);
-    {
-      uint8_t* ob = reinterpret_cast<uint8_t*>(pr.O) + ((size_t)wrow0 * pr.ldo + wcol0) * sizeof(T);
-#pragma unroll
-      for (int it = 0; it < 32; ++it) {
-        const int idx = it * 64 + lane, r = idx >> 4, ch = idx & 15;
-        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(reg + r * kEpiStride + ch * 16);
-        st_global<u32x4_t>(ob + (size_t)r * pr.ldo * sizeof(T) + ch * 16, x);
-      }
-    }
-    // Transposed layout: X'^T for kApply, the mirrored tile for the Gram products.
-    if (MODE == kApply || mirror) {
+            for (int e = 0; e < 4; ++e)
+              *reinterpret_cast<uint16_t*>(reg + (i * 32 + g * 8 + lg + e) * kEpiStride +
+                                           (j * 32 + lc) * 2) = f32_to_bf16(acc[i][j][4 * g + e]);
+    };
+    auto lds_transposed = [&]() {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -439,15 +433,55 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
             o[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
             *reinterpret_cast<u32x2_t*>(reg + (j * 32 + lc) * kEpiStride + (i * 32 + g * 8 + lg) * 2) = o;
           }
-      uint8_t* tb = (MODE == kApply)
-                        ? reinterpret_cast<uint8_t*>(pr.OT) + ((size_t)wcol0 * pr.ldot + wrow0) * sizeof(T)
-                        : reinterpret_cast<uint8_t*>(pr.O) + ((size_t)wcol0 * pr.ldo + wrow0) * sizeof(T);
-      const size_t tld = (size_t)((MODE == kApply) ? pr.ldot : pr.ldo) * sizeof(T);
+    };
+    // LDS row rr -> dst + rr * ld (elements); whole, aligned 256-B rows.
+    auto store_rows = [&](uint8_t* dst, size_t ld) {
 #pragma unroll
       for (int it = 0; it < 32; ++it) {
-        const int idx = it * 64 + lane, c = idx >> 4, ch = idx & 15;
-        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(reg + c * kEpiStride + ch * 16);
-        st_global<u32x4_t>(tb + (size_t)c * tld + ch * 16, x);
+        const int idx = it * 64 + lane, r = idx >> 4, ch = idx & 15;
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(reg + r * kEpiStride + ch * 16);
+        st_global<u32x4_t>(dst + ((size_t)r * ld) * sizeof(T) + ch * 16, x);
+      }
+    };
+    if constexpr (MODE == kApplyLast) {
+      // u, compact, in the matrix's own orientation: [um x un] (row-major
+      // pass) or, for a tall matrix, [un x um] (transposed pass); rows and
+      // columns past the valid dims are dropped.
+      int rbase, cbase, nrow, ncol, ld;
+      if (!pr.u_tall) {
+        lds_rowmajor();
+        rbase = wrow0; cbase = wcol0; nrow = pr.um; ncol = pr.un; ld = pr.un;
+      } else {
+        lds_transposed();
+        rbase = wcol0; cbase = wrow0; nrow = pr.un; ncol = pr.um; ld = pr.um;
+      }
+      uint16_t* U = reinterpret_cast<uint16_t*>(pr.U);
+      const bool vec_ok = (ld & 7) == 0;
+#pragma unroll 4
+      for (int it = 0; it < 32; ++it) {
+        const int idx = it * 64 + lane, r = idx >> 4, c0 = (idx & 15) * 8;
+        const int gr = rbase + r, gc = cbase + c0;
+        if (gr >= nrow || gc >= ncol) continue;
+        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(reg + r * kEpiStride + c0 * 2);
+        uint16_t* d = U + (size_t)gr * ld + gc;
+        if (vec_ok && gc + 8 <= ncol) {
+          st_global<u32x4_t>(d, x);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (gc + q < ncol) st_global<uint16_t>(d + q, (uint16_t)(x[q >> 1] >> (16 * (q & 1))));
+        }
+      }
+    } else {
+      lds_rowmajor();
+      store_rows(reinterpret_cast<uint8_t*>(pr.O) + ((size_t)wrow0 * pr.ldo + wcol0) * sizeof(T), pr.ldo);
+      // Transposed layout: X'^T for kApply, the mirrored tile for the Gram products.
+      if (MODE == kApply || mirror) {
+        lds_transposed();
+        if (MODE == kApply)
+          store_rows(reinterpret_cast<uint8_t*>(pr.OT) + ((size_t)wcol0 * pr.ldot + wrow0) * sizeof(T), pr.ldot);
+        else
+          store_rows(reinterpret_cast<uint8_t*>(pr.O) + ((size_t)wcol0 * pr.ldo + wrow0) * sizeof(T), pr.ldo);
       }
     }
   } else {

@@ -309,7 +309,7 @@ struct muonh_handle {
   bool ev_pending[kRing] = {false, false, false, false};
   int ev_next = 0;
   int ev_cur = 0;
-  double phase_total[6] = {0, 0, 0, 0, 0, 0};
+  double phase_total[7] = {0, 0, 0, 0, 0, 0, 0};
   int32_t timed_steps = 0;
 
   template <typename T> T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
@@ -364,10 +364,12 @@ int fold_events(muonh_handle* h, int k) {
   if ((rc = el(0, 1, &h->phase_total[0]))) return rc;
   size_t e = 1;
   for (int it = 0; it < S; ++it)
-    for (int k3 = 0; k3 < 3; ++k3, ++e)
-      if ((rc = el(e, e + 1, &h->phase_total[1 + k3]))) return rc;
-  if ((rc = el(e, e + 1, &h->phase_total[4]))) return rc;
-  if ((rc = el(e + 1, e + 2, &h->phase_total[5]))) return rc;
+    for (int k3 = 0; k3 < 3; ++k3, ++e) {
+      const int ph = (k3 == 2 && it == S - 1) ? 4 : 1 + k3;   // last B X launch apart
+      if ((rc = el(e, e + 1, &h->phase_total[ph]))) return rc;
+    }
+  if ((rc = el(e, e + 1, &h->phase_total[5]))) return rc;
+  if ((rc = el(e + 1, e + 2, &h->phase_total[6]))) return rc;
   h->ev_pending[k] = false;
   h->timed_steps++;
   return MUONH_OK;
@@ -747,14 +749,14 @@ int muonh_set_timing(muonh_handle* h, int32_t enable) {
 
 int muonh_get_timing(muonh_handle* h, float* phases_ms, int32_t n_phases, int32_t* n_steps) {
   if (!h || !phases_ms || !n_steps) return fail(MUONH_EINVAL, "null argument");
-  if (n_phases < 6) return fail(MUONH_EINVAL, "need room for 6 phases");
+  if (n_phases < 7) return fail(MUONH_EINVAL, "need room for 7 phases");
   // Fold the pending sets oldest first.
   for (int j = 0; j < muonh_handle::kRing; ++j) {
     const int k = (h->ev_next + j) % muonh_handle::kRing;
     const int rc = fold_events(h, k);
     if (rc) return rc;
   }
-  for (int k = 0; k < n_phases; ++k) phases_ms[k] = k < 6 ? (float)h->phase_total[k] : 0.0f;
+  for (int k = 0; k < n_phases; ++k) phases_ms[k] = k < 7 ? (float)h->phase_total[k] : 0.0f;
   *n_steps = h->timed_steps;
   for (double& t : h->phase_total) t = 0.0;
   h->timed_steps = 0;
