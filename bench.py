@@ -41,7 +41,8 @@ def per_kernel_work(shapes, ns_steps, tsize, gsize):
     NS products per matrix and iteration (m = min side, n = max side):
       X X^T: 2 m^2 n,  A A: 2 m^3,  B X: 2 m^2 n  (dense counts).
     Elementwise bytes per matrix (p = rows*cols, padded NS area q = m_pad*n_pad):
-      momentum: read G (gsize p) + read/write M (8 p) + write X_0 and X_0^T (2 tsize q)
+      momentum: read G (gsize p) + read/write M (8 p) + write X_0 (tsize q; the fp32
+                path also writes X_0^T, another tsize q)
       reduce:   read W (4 p) + read u (tsize p)
       update:   read/write W (8 p) + read u (tsize p)
     """
@@ -58,7 +59,7 @@ def per_kernel_work(shapes, ns_steps, tsize, gsize):
         p = r * c
         q = pad(m) * pad(n)
         params += p
-        b["momentum"] += gsize * p + 8 * p + 2 * tsize * q
+        b["momentum"] += gsize * p + 8 * p + (1 if tsize == 2 else 2) * tsize * q
         b["reduce"] += 4 * p + tsize * p
         b["update"] += 8 * p + tsize * p
     return f, b, params

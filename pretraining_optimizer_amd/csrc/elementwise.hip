@@ -79,51 +79,67 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, const MatGeom& g
   const int cc = (tid & 15) * 4;
   const int rr = tid >> 4;
   const int64_t r0 = (int64_t)t.tr * kMomTile, c0 = (int64_t)t.tc * kMomTile;
-  T* D = reinterpret_cast<T*>(g.tall ? g.XT[0] : g.X[0]);   // same orientation as M
-  T* Tr = reinterpret_cast<T*>(g.tall ? g.X[0] : g.XT[0]);  // transposed
+  // X_0 in M's orientation (D) and transposed (Tr); the bf16 plan keeps only
+  // X (no X^T), so one of the two is absent.
+  T* D = reinterpret_cast<T*>(g.tall ? g.XT[0] : g.X[0]);
+  T* Tr = reinterpret_cast<T*>(g.tall ? g.X[0] : g.XT[0]);
   const int64_t ldD = g.c_pad + g.ld_skew, ldT = g.r_pad + g.ld_skew;
   const bool vec_ok = (g.cols & 3) == 0;
   const float beta = prm.beta;
   float ss = 0.0f;
 
+  // All loads of the thread's four rows are issued before the first store
+  // (M is written in place, so the compiler may not hoist them itself).
+  f32x4_t gv[4], mv[4];
+  bool full[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t row = r0 + rr + 16 * q;
+    const int64_t col = c0 + cc;
+    full[q] = row < g.rows && vec_ok && col + 3 < g.cols;
+    if (full[q]) {
+      const int64_t off = row * g.cols + col;
+      gv[q] = GradLoad<G>::load4(p.g, off);
+      mv[q] = Vec4<float>::load(p.m + off);
+    }
+  }
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int64_t row = r0 + rr + 16 * q;
     const int64_t col = c0 + cc;
     f32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (row < g.rows) {
-      const int64_t off = row * g.cols + col;
-      if (vec_ok && col + 3 < g.cols) {
-        const f32x4_t gv = GradLoad<G>::load4(p.g, off);
-        f32x4_t mv = Vec4<float>::load(p.m + off);
-        mv = beta * mv + gv;
-        Vec4<float>::store(p.m + off, mv);
-        y = prm.nesterov ? gv + beta * mv : mv;
-      } else {
+    const int64_t off = row * g.cols + col;
+    if (full[q]) {
+      const f32x4_t m = beta * mv[q] + gv[q];
+      Vec4<float>::store(p.m + off, m);
+      y = prm.nesterov ? gv[q] + beta * m : m;
+    } else if (row < g.rows) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (col + e < g.cols) {
-            const float gv = GradLoad<G>::load1(p.g, off + e);
-            const float mv = beta * p.m[off + e] + gv;
-            p.m[off + e] = mv;
-            y[e] = prm.nesterov ? gv + beta * mv : mv;
-          }
+      for (int e = 0; e < 4; ++e) {
+        if (col + e < g.cols) {
+          const float gs = GradLoad<G>::load1(p.g, off + e);
+          const float ms = beta * p.m[off + e] + gs;
+          p.m[off + e] = ms;
+          y[e] = prm.nesterov ? gs + beta * ms : ms;
         }
       }
     }
     ss += y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
+    if (Tr)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tile[rr + 16 * q][cc + e] = y[e];
-    Vec4<T>::store(D + row * ldD + col, y);
+      for (int e = 0; e < 4; ++e) tile[rr + 16 * q][cc + e] = y[e];
+    if (D) Vec4<T>::store(D + row * ldD + col, y);
   }
-  __syncthreads();
+  if (Tr) {
+    __syncthreads();
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int oc = rr + 16 * q;  // column of the source tile = row of the transposed output
-    f32x4_t y;
+    for (int q = 0; q < 4; ++q) {
+      const int oc = rr + 16 * q;  // column of the source tile = row of the transposed output
+      f32x4_t y;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) y[e] = tile[cc + e][oc];
-    Vec4<T>::store(Tr + (c0 + oc) * ldT + r0 + cc, y);
+      for (int e = 0; e < 4; ++e) y[e] = tile[cc + e][oc];
+      Vec4<T>::store(Tr + (c0 + oc) * ldT + r0 + cc, y);
+    }
   }
   double v[1] = {(double)ss};
   block_sum<1>(v, red);
@@ -277,15 +293,30 @@ __global__ __launch_bounds__(kElemThreads) void update_kernel(const Chunk* __res
   const float k1 = scal[c.mat].k1, k2 = scal[c.mat].k2;
   const int tid = threadIdx.x;
   const int n4 = c.len & ~3;
-  for (int i = tid * 4; i < n4; i += kElemThreads * 4) {
+  // Batches of 4 x 4 elements per thread: every load of a batch is issued
+  // before its stores (W is written in place, so the compiler may not hoist
+  // loads across them itself).
+  constexpr int kStep = kElemThreads * 4;
+  int i = tid * 4;
+  for (; i + 3 * kStep < n4; i += 4 * kStep) {
+    f32x4_t w[4], u[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      w[k] = Vec4<float>::load(W + i + k * kStep);
+      u[k] = Vec4<T>::load(U + i + k * kStep);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) Vec4<float>::store(W + i + k * kStep, k1 * w[k] - k2 * u[k]);
+  }
+  for (; i < n4; i += kStep) {
     const f32x4_t w = Vec4<float>::load(W + i);
     const f32x4_t u = Vec4<T>::load(U + i);
     Vec4<float>::store(W + i, k1 * w - k2 * u);
   }
-  for (int i = n4 + tid; i < c.len; i += kElemThreads) {
+  for (int j = n4 + tid; j < c.len; j += kElemThreads) {
     float u;
-    if constexpr (sizeof(T) == 2) u = bf16_to_f32(U[i]); else u = U[i];
-    W[i] = k1 * W[i] - k2 * u;
+    if constexpr (sizeof(T) == 2) u = bf16_to_f32(U[j]); else u = U[j];
+    W[j] = k1 * W[j] - k2 * u;
   }
 }
 

@@ -12,20 +12,26 @@
 // Every product is written as C = P Q^T with both operands row-major and the
 // contraction index contiguous, so both MFMA operands are read the same way:
 //   kGram : P = Q = X;   kPoly : P = Q = A (A is symmetric);
-//   kApply: P = B, Q = X^T (the iterate is kept in both layouts).
+//   kApply: P = B' (symmetric), Q = X^T (fp32: a stored copy; bf16: X read
+//           through transposing LDS reads, below).
 //
 // Work decomposition: a 256 x 256 output tile per workgroup of 4 wavefronts
-// (2 x 2, each 128 x 128 = 4 x 4 MFMA blocks of 32 x 32).  K advances in
-// stages of 64 bytes per row (32 bf16 / 16 fp32) through an LDS ring filled
-// by direct-to-LDS loads
-// (global_load_lds_dwordx4: no staging registers) ring of 5 stages
-// (5 x 32 KiB = the whole 160 KiB LDS), issued three stages ahead of the MFMAs
-// that read them, with one barrier per stage placed mid-stage so the next
-// stage's first operand fragments are read while the current stage's second
-// half runs on the MFMA pipe.  LDS rows keep
-// their 16-byte chunks XOR-swizzled per row (through each lane's global
-// address), so the 32-row MFMA operand reads are free of bank conflicts
-// without padding.
+// (2 x 2, each 128 x 128 = 4 x 4 MFMA blocks of 32 x 32, 256 fp32
+// accumulators per lane).  K advances in stages of 128 bytes per operand row
+// (64 bf16 / 32 fp32): global loads of whole 128-byte lines into registers
+// three stages ahead, LDS writes one stage ahead into a 2-slot ring (2 x 64
+// KiB), and one barrier per stage, placed before its last 16-deep sub-step so
+// that the next stage's first fragments are read while that sub-step runs.
+// Loads, LDS writes and fragment reads are spread between the MFMAs so the
+// in-order issue never parks the MFMA pipe behind a memory queue.  LDS rows
+// keep their 16-byte chunks XOR-swizzled per row, so the 32-row MFMA operand
+// reads are free of bank conflicts without padding.
+//
+// bf16 B' X reads X in its own row-major layout: a stage of that operand is
+// 64 rows (k) x 256 columns (n), and the MFMA B fragments come out of LDS
+// through the transposing read ds_read_b64_tr_b16 (one 16-lane group turns
+// 4 rows x 16 columns into 16 lanes x 4 k).  The iterate is then stored once
+// (no X^T copy) and B' X writes one layout.  The fp32 path keeps X and X^T.
 //
 // The host builds the tile list: for the symmetric products only the upper
 // tiles are listed and each off-diagonal tile also writes its mirror, and the
@@ -40,17 +46,17 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
-// Operand path: register-staged loads of whole 128-byte row segments into a
-// 2-slot LDS ring (true), or direct-to-LDS loads of 64-byte row segments
-// into a 5-slot ring (false).
-constexpr bool kRegStaged = true;
-constexpr int kRowBytes = kRegStaged ? 128 : 64;     // one K stage of one row
-constexpr int kStages = kRegStaged ? 2 : 5;          // LDS ring depth
-constexpr int kOperandBytes = kGemmTile * kRowBytes; // 32 KiB / 16 KiB
+constexpr int kRowBytes = 128;                       // one K stage of one operand row
+constexpr int kStages = 2;                           // LDS ring depth
+constexpr int kOperandBytes = kGemmTile * kRowBytes; // 32 KiB
 constexpr int kStageBytes = 2 * kOperandBytes;       // P and Q
 constexpr int kSubsteps = kRowBytes / 32;            // 16-deep MFMA steps per stage
-constexpr int kDmaPerOperand = 4;                    // 1 KiB per DMA instruction per wave
+// K-major Q operand (bf16 B' X): 64 rows of 256 columns per stage.
+constexpr int kTrRows = kRowBytes / 2;               // k rows per stage
+constexpr int kTrPitch = kGemmTile * 2;              // 512 B per LDS row
+static_assert(kTrRows * kTrPitch == kOperandBytes, "both Q layouts fill one operand slot");
 // The bf16 epilogue stages each wavefront's 128 x 128 sub-tile in its own
 // region of 128 rows x (256 + 16) bytes.
 constexpr int kEpiStride = 272;
@@ -60,16 +66,21 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one CU");
 
 #define MUONH_LDS __attribute__((address_space(3)))
 
-// Chunk c of LDS row r sits at 16-byte slot c ^ swz(r).  For a 16-byte read
-// of one chunk by 32 consecutive rows this is free of bank conflicts whether
-// the LDS serves 8 lanes (32 banks) or 16 lanes (64 banks) per cycle.
-__device__ __forceinline__ int swz64(int r) { return ((r >> 1) ^ (r >> 2)) & 3; }    // 4 chunks/row
-__device__ __forceinline__ int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }    // 8 chunks/row
-__device__ __forceinline__ int swz_row(int r) { return kRegStaged ? swz128(r) : swz64(r); }
+// Chunk c of a 128-byte LDS row r sits at 16-byte slot c ^ swz128(r).  For a
+// 16-byte read of one chunk by 32 consecutive rows this is free of bank
+// conflicts whether the LDS serves 8 lanes (32 banks) or 16 lanes (64 banks)
+// per cycle.
+__device__ __forceinline__ int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// Chunk c of a 512-byte K-major row k sits at slot c ^ swz_tr(k).  A
+// transposing read has each 16-lane group fetch 4 consecutive rows x 32
+// bytes, two groups side by side: with these offsets the 16 (row, chunk)
+// pairs of two groups fall in distinct banks (64 banks, 32 lanes per cycle)
+// and those of one group in distinct banks (32 banks, 16 lanes per cycle).
+__device__ __forceinline__ int swz_tr(int k) { return (4 * (k & 1)) ^ (10 * ((k >> 1) & 1)); }
 
-// Workgroup barrier without a memory fence (the fence would drain every
-// in-flight LDS-DMA load); the empty asm statements keep the compiler from
-// moving LDS accesses across it.
+// Workgroup barrier without a memory fence (a fence would also wait for the
+// global loads in flight into registers); the empty asm statements keep the
+// compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -83,6 +94,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (63 << 8));
   asm volatile("" ::: "memory");
 }
+
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100, kSgDsWrite = 0x200;
+#define MUONH_SG(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 // One 16-byte LDS operand fragment x one 16-byte fragment -> 32x32 block.
 template <typename T> struct Mfma;
@@ -142,17 +157,42 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 
   // MFMA operand rows: 32 consecutive rows per block; (row & 15) == (lane & 15).
   // Sub-step s reads 16-byte chunk 2s (lanes 0-31) / 2s+1 (lanes 32-63).
-  const int swz = swz_row(lane & 15);
+  const int swz = swz128(lane & 15);
   const int a_off = (wr * 128 + (lane & 31)) * kRowBytes;
   const int b_off = kOperandBytes + (wc * 128 + (lane & 31)) * kRowBytes;
+  // K-major B fragments (kQT): lane l of 16-lane group g = l / 16 fetches the
+  // 8 bytes at row 16 s + 4 h + 8 (g / 2) + (l % 16) / 4 of the stage and
+  // column 32 j + 16 (g % 2) + 4 (l % 4) of the wavefront's 128 columns; the
+  // transposing read then hands lane l the 4 consecutive k of column
+  // 32 j + l % 32 (h = 0: the first 4 of the lane's 8 k, h = 1: the last 4).
+  constexpr bool kQT = sizeof(T) == 2 && (MODE == kApply || MODE == kApplyLast);
+  const int tr_k = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_c = wc * 16 + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+  int tr_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    tr_off[j] = kOperandBytes + tr_k * kTrPitch + (((tr_c + 4 * j) ^ swz_tr(tr_k)) << 4) + (lane & 1) * 8;
   auto load_frag = [&](u32x4_t (&a)[4], u32x4_t (&b)[4], int slot, int s) {
     const uint8_t* st = smem + slot * kStageBytes + (((s * 2 + (lane >> 5)) ^ swz) << 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       a[i] = *reinterpret_cast<const u32x4_t*>(st + a_off + i * 32 * kRowBytes);
+    if constexpr (kQT) {
+      MUONH_LDS uint8_t* sq = lds + slot * kStageBytes + s * 16 * kTrPitch;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const u32x4_t*>(st + b_off + j * 32 * kRowBytes);
+      for (int j = 0; j < 4; ++j) {
+        const u32x2_t lo = __builtin_bit_cast(
+            u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((MUONH_LDS i16x4_t*)(sq + tr_off[j])));
+        const u32x2_t hi = __builtin_bit_cast(
+            u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                         (MUONH_LDS i16x4_t*)(sq + tr_off[j] + 4 * kTrPitch)));
+        b[j] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const u32x4_t*>(st + b_off + j * 32 * kRowBytes);
+    }
   };
   auto mma = [&](const u32x4_t (&a)[4], const u32x4_t (&b)[4]) {
 #pragma unroll
@@ -160,173 +200,148 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) Mfma<T>::run(acc[i][j], a[i], b[j]);
   };
-  // Scheduling of one sub-step: the 8 fragment reads of the next sub-step
-  // are interleaved one per MFMA with the first 8 of the current 16 MFMAs,
-  // so at most 8 LDS reads are in flight (lgkmcnt stays exact) and each read
-  // has >= 8 MFMAs (>= 256 cycles) to land before it is used.
-  auto interleave = [&]() {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     // 8 MFMAs
-  };
   u32x4_t fa0[4], fb0[4], fa1[4], fb1[4];
 
-  if constexpr (kRegStaged) {
-    // Thread t owns rows (i*32 + t/8) and 16-byte chunk t%8 of each operand,
-    // so one load instruction of a wavefront covers 8 whole 128-byte lines.
-    // Stage s is loaded into one of two register sets during stage s-3 (P
-    // half in sub-step 1, Q half in sub-step 2), written to LDS slot s%2
-    // during stage s-1 (P in sub-step 0, Q in sub-step 1) and published by
-    // the barrier that stage s-1 places before its last sub-step.  Loads and
-    // LDS writes are spread one per MFMA or two so the in-order issue never
-    // stalls the MFMA pipe behind a full memory queue.
-    static_assert(kSubsteps == 4, "the stage schedule below assumes 4 sub-steps");
-    constexpr int kLd = kOperandBytes / 16 / kGemmThreads;   // 8 loads per operand
-    const int srow = tid >> 3, schunk = tid & 7;
-    const uint8_t* pg = reinterpret_cast<const uint8_t*>(pr.P) + (size_t)(row0 + srow) * pstride + schunk * 16;
-    const uint8_t* qg = reinterpret_cast<const uint8_t*>(pr.Q) + (size_t)(col0 + srow) * qstride + schunk * 16;
-    const int sst = srow * kRowBytes + ((schunk ^ swz128(srow & 15)) << 4);
-    u32x4_t ra0[kLd], rb0[kLd], ra1[kLd], rb1[kLd];
-    auto gload_half = [&](u32x4_t (&r)[kLd], const uint8_t* g, size_t stride, int kt) {
-      const size_t koff = (size_t)min(kt, nk - 1) * kRowBytes;   // tail: reload the last stage
+  // Thread t owns rows (i*32 + t/8) and 16-byte chunk t%8 of a row-major
+  // operand, so one load instruction of a wavefront covers 8 whole 128-byte
+  // lines; of a K-major Q operand it owns rows (i*8 + t/32) and chunk t%32
+  // (2 whole 512-byte row segments per instruction).  Stage s is loaded into
+  // one of two register sets during stage s-3 (P half in sub-step 1, Q half
+  // in sub-step 2), written to LDS slot s%2 during stage s-1 (P in sub-step
+  // 0, Q in sub-step 1) and published by the barrier that stage s-1 places
+  // before its last sub-step.
+  static_assert(kSubsteps == 4, "the stage schedule below assumes 4 sub-steps");
+  constexpr int kLd = kOperandBytes / 16 / kGemmThreads;   // 8 loads per operand
+  const int srow = tid >> 3, schunk = tid & 7;
+  const int qrow = tid >> 5, qchunk = tid & 31;
+  const uint8_t* pg = reinterpret_cast<const uint8_t*>(pr.P) + (size_t)(row0 + srow) * pstride + schunk * 16;
+  const uint8_t* qg = kQT ? reinterpret_cast<const uint8_t*>(pr.Q) + (size_t)qrow * qstride +
+                                (size_t)col0 * sizeof(T) + qchunk * 16
+                          : reinterpret_cast<const uint8_t*>(pr.Q) + (size_t)(col0 + srow) * qstride + schunk * 16;
+  const int sst = srow * kRowBytes + ((schunk ^ swz128(srow & 15)) << 4);
+  const int sstq = kQT ? qrow * kTrPitch + ((qchunk ^ swz_tr(qrow)) << 4) : sst;
+  u32x4_t ra0[kLd], rb0[kLd], ra1[kLd], rb1[kLd];
+  // Stages past the last one (the pipeline's tail) reload the last stage.
+  auto gload_p = [&](u32x4_t (&r)[kLd], int kt) {
+    const size_t koff = (size_t)min(kt, nk - 1) * kRowBytes;
 #pragma unroll
-      for (int i = 0; i < kLd; ++i) r[i] = ld_global<u32x4_t>(g + (size_t)(i * 32) * stride + koff);
-    };
-    auto sstore_half = [&](const u32x4_t (&r)[kLd], int slot, int operand) {
-      uint8_t* st = smem + slot * kStageBytes + operand * kOperandBytes + sst;
+    for (int i = 0; i < kLd; ++i) r[i] = ld_global<u32x4_t>(pg + (size_t)(i * 32) * pstride + koff);
+  };
+  auto gload_q = [&](u32x4_t (&r)[kLd], int kt) {
+    if constexpr (kQT) {
+      const size_t k0 = (size_t)min(kt, nk - 1) * kTrRows;
 #pragma unroll
-      for (int i = 0; i < kLd; ++i) *reinterpret_cast<u32x4_t*>(st + i * 32 * kRowBytes) = r[i];
-    };
-    // s_waitcnt lgkmcnt(0) alone: this wavefront's LDS accesses are done.
-    auto wait_lds = [&]() {
-      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
-      asm volatile("" ::: "memory");
-    };
-    // One K stage read from LDS slot `cur`; register set (ra, rb) holds the
-    // next stage, which goes to slot `nxt`, and is then refilled with stage
-    // kt_load.  On entry fa0/fb0 hold sub-step 0 of this stage; on exit they
-    // hold sub-step 0 of the next stage.
-    auto stage = [&](u32x4_t (&ra)[kLd], u32x4_t (&rb)[kLd], int cur, int nxt, int kt_load) {
-      // sub-step 0: MFMA, frag read, MFMA, LDS write (P half of the next stage)
-      load_frag(fa1, fb1, cur, 1);
-      mma(fa0, fb0);
-      sstore_half(ra, nxt, 0);
+      for (int i = 0; i < kLd; ++i) r[i] = ld_global<u32x4_t>(qg + (k0 + i * 8) * qstride);
+    } else {
+      const size_t koff = (size_t)min(kt, nk - 1) * kRowBytes;
+#pragma unroll
+      for (int i = 0; i < kLd; ++i) r[i] = ld_global<u32x4_t>(qg + (size_t)(i * 32) * qstride + koff);
+    }
+  };
+  // Row i of this thread's share sits 4 KiB further in either Q layout.
+  auto sstore = [&](const u32x4_t (&r)[kLd], int slot, int operand) {
+    uint8_t* st = smem + slot * kStageBytes + operand * kOperandBytes + (operand ? sstq : sst);
+#pragma unroll
+    for (int i = 0; i < kLd; ++i) *reinterpret_cast<u32x4_t*>(st + i * 4096) = r[i];
+  };
+  // s_waitcnt lgkmcnt(0) alone: this wavefront's LDS accesses are done.
+  auto wait_lds = [&]() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+    asm volatile("" ::: "memory");
+  };
+  // One K stage read from LDS slot `cur`; register set (ra, rb) holds the
+  // next stage, which goes to slot `nxt`, and is then refilled with stage
+  // kt_load.  On entry fa0/fb0 hold sub-step 0 of this stage; on exit they
+  // hold sub-step 0 of the next stage.  Each sub-step's 16 MFMAs are
+  // interleaved with the next sub-step's fragment reads (8, or 12 with
+  // K-major B fragments), the LDS writes and the global loads, a few at a
+  // time, so no read waits long and the MFMA pipe stays fed.
+  auto stage = [&](u32x4_t (&ra)[kLd], u32x4_t (&rb)[kLd], int cur, int nxt, int kt_load) {
+    // sub-step 0: + LDS writes of the P half of the next stage
+    load_frag(fa1, fb1, cur, 1);
+    mma(fa0, fb0);
+    sstore(ra, nxt, 0);
+    if constexpr (kQT) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        MUONH_SG(kSgMfma, 1); MUONH_SG(kSgDsRead, 2); MUONH_SG(kSgMfma, 1); MUONH_SG(kSgDsRead, 1);
+        MUONH_SG(kSgDsWrite, 1); MUONH_SG(kSgMfma, 1); MUONH_SG(kSgDsWrite, 1); MUONH_SG(kSgMfma, 1);
+      }
+    } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        MUONH_SG(kSgMfma, 1); MUONH_SG(kSgDsRead, 1); MUONH_SG(kSgMfma, 1); MUONH_SG(kSgDsWrite, 1);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // sub-step 1: + LDS writes of the Q half, refill of the P half
-      load_frag(fa0, fb0, cur, 2);
-      mma(fa1, fb1);
-      sstore_half(rb, nxt, 1);
-      gload_half(ra, pg, pstride, kt_load);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // sub-step 1: + LDS writes of the Q half, refill of the P half
+    load_frag(fa0, fb0, cur, 2);
+    mma(fa1, fb1);
+    sstore(rb, nxt, 1);
+    gload_p(ra, kt_load);
+    if constexpr (kQT) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        MUONH_SG(kSgMfma, 1); MUONH_SG(kSgDsRead, 1); MUONH_SG(kSgDsWrite, 1); MUONH_SG(kSgMfma, 1);
+        MUONH_SG(kSgVmemRead, 1); MUONH_SG(kSgDsRead, 1); MUONH_SG(kSgMfma, 1); MUONH_SG(kSgDsWrite, 1);
+        MUONH_SG(kSgVmemRead, 1); MUONH_SG(kSgDsRead, 1); MUONH_SG(kSgMfma, 1);
+      }
+    } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        MUONH_SG(kSgMfma, 1); MUONH_SG(kSgDsRead, 1); MUONH_SG(kSgDsWrite, 1); MUONH_SG(kSgMfma, 1);
+        MUONH_SG(kSgVmemRead, 1);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // sub-step 2: + refill of the Q half
-      load_frag(fa1, fb1, cur, 3);
-      mma(fa0, fb0);
-      gload_half(rb, qg, qstride, kt_load);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // sub-step 2: + refill of the Q half
+    load_frag(fa1, fb1, cur, 3);
+    mma(fa0, fb0);
+    gload_q(rb, kt_load);
+    if constexpr (kQT) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        MUONH_SG(kSgMfma, 1); MUONH_SG(kSgDsRead, 1); MUONH_SG(kSgVmemRead, 1); MUONH_SG(kSgMfma, 1);
+        MUONH_SG(kSgDsRead, 1); MUONH_SG(kSgMfma, 1); MUONH_SG(kSgVmemRead, 1); MUONH_SG(kSgDsRead, 1);
+        MUONH_SG(kSgMfma, 1);
+      }
+    } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        MUONH_SG(kSgMfma, 1); MUONH_SG(kSgDsRead, 1); MUONH_SG(kSgMfma, 1); MUONH_SG(kSgVmemRead, 1);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // the next stage is in LDS; every wavefront has its last fragments of
-      // this stage in registers, so slot `cur` may be rewritten after this
-      wait_lds();
-      lds_barrier();
-      // sub-step 3: + fragments of the next stage's sub-step 0
-      load_frag(fa0, fb0, nxt, 0);
-      mma(fa1, fb1);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    gload_half(ra0, pg, pstride, 0);
-    gload_half(rb0, qg, qstride, 0);
-    gload_half(ra1, pg, pstride, 1);
-    gload_half(rb1, qg, qstride, 1);
-    sstore_half(ra0, 0, 0);    // stage 0 -> slot 0
-    sstore_half(rb0, 0, 1);
-    gload_half(ra0, pg, pstride, 2);
-    gload_half(rb0, qg, qstride, 2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // the next stage is in LDS; every wavefront has its last fragments of
+    // this stage in registers, so slot `cur` may be rewritten after this
     wait_lds();
     lds_barrier();
-    load_frag(fa0, fb0, 0, 0);
-    // nk is even: two stages per trip, register sets alternating.
-    for (int kt = 0; kt < nk; kt += 2) {
-      stage(ra1, rb1, 0, 1, kt + 3);   // stage kt   (slot 0); set 1 = stage kt+1
-      stage(ra0, rb0, 1, 0, kt + 4);   // stage kt+1 (slot 1); set 0 = stage kt+2
-    }
-  } else {
-    // Direct-to-LDS loads: one global_load_lds_dwordx4 writes 64 lanes x 16 B
-    // = 16 LDS rows of 64 B, lane L landing in row L/4, slot L%4.  Each lane
-    // therefore fetches global chunk (L%4) ^ swz64(row) of its row.  Wave w
-    // fills row blocks w, w+4, w+8, w+12 (16 rows each) of each operand.
-    const int drow = lane >> 2;
-    const int dchunk = (lane & 3) ^ swz64(drow);
-    const uint8_t* pdma = reinterpret_cast<const uint8_t*>(pr.P) +
-                          (size_t)(row0 + wave * 16 + drow) * pstride + dchunk * 16;
-    const uint8_t* qdma = reinterpret_cast<const uint8_t*>(pr.Q) +
-                          (size_t)(col0 + wave * 16 + drow) * qstride + dchunk * 16;
-    auto issue = [&](int kt, int slot) {
-      MUONH_LDS uint8_t* st = lds + slot * kStageBytes + wave * 16 * kRowBytes;
-      const size_t koff = (size_t)kt * kRowBytes;
+    // sub-step 3: + fragments of the next stage's sub-step 0, read early
+    load_frag(fa0, fb0, nxt, 0);
+    mma(fa1, fb1);
+    constexpr int kReads = kQT ? 12 : 8;
 #pragma unroll
-      for (int i = 0; i < kDmaPerOperand; ++i) {
-        __builtin_amdgcn_global_load_lds(
-            (const MUONH_GLOBAL void*)(pdma + (size_t)(i * 64) * pstride + koff),
-            (MUONH_LDS void*)(st + i * 64 * kRowBytes), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(
-            (const MUONH_GLOBAL void*)(qdma + (size_t)(i * 64) * qstride + koff),
-            (MUONH_LDS void*)(st + kOperandBytes + i * 64 * kRowBytes), 16, 0, 0);
-      }
-    };
-    auto wait_stage = [&](int ahead) {
-      if (ahead >= 2) wait_vmcnt<4 * kDmaPerOperand>();
-      else if (ahead == 1) wait_vmcnt<2 * kDmaPerOperand>();
-      else wait_vmcnt<0>();
-    };
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
-    issue(3, 3);
-    wait_vmcnt<6 * kDmaPerOperand>();   // stage 0 landed, stages 1-3 in flight
-    lds_barrier();
-    load_frag(fa0, fb0, 0, 0);
-    int slot = 0;
-    for (int kt = 0; kt < nk; ++kt) {
-      const int next = (slot == kStages - 1) ? 0 : slot + 1;
-      load_frag(fa1, fb1, slot, 1);
-      mma(fa0, fb0);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
-      wait_stage(min(kt + 3, nk - 1) - (kt + 1));
-      lds_barrier();
-      if (kt + 4 < nk) issue(kt + 4, (slot == 0) ? kStages - 1 : slot - 1);
-      __builtin_amdgcn_sched_barrier(0);
-      load_frag(fa0, fb0, next, 0);
-      mma(fa1, fb1);
-      interleave();
-      __builtin_amdgcn_sched_barrier(0);
-      slot = next;
+    for (int k = 0; k < kReads; ++k) {
+      MUONH_SG(kSgMfma, 1); MUONH_SG(kSgDsRead, 1);
     }
+    MUONH_SG(kSgMfma, 16 - kReads);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  gload_p(ra0, 0);
+  gload_q(rb0, 0);
+  gload_p(ra1, 1);
+  gload_q(rb1, 1);
+  sstore(ra0, 0, 0);    // stage 0 -> slot 0
+  sstore(rb0, 0, 1);
+  gload_p(ra0, 2);
+  gload_q(rb0, 2);
+  wait_lds();
+  lds_barrier();
+  load_frag(fa0, fb0, 0, 0);
+  // nk is even: two stages per trip, register sets alternating.
+  for (int kt = 0; kt < nk; kt += 2) {
+    stage(ra1, rb1, 0, 1, kt + 3);   // stage kt   (slot 0); set 1 = stage kt+1
+    stage(ra0, rb0, 1, 0, kt + 4);   // stage kt+1 (slot 1); set 0 = stage kt+2
   }
   wait_vmcnt<0>();   // no load in flight into LDS or registers past this point
 
@@ -475,13 +490,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     } else {
       lds_rowmajor();
       store_rows(reinterpret_cast<uint8_t*>(pr.O) + ((size_t)wrow0 * pr.ldo + wcol0) * sizeof(T), pr.ldo);
-      // Transposed layout: X'^T for kApply, the mirrored tile for the Gram products.
-      if (MODE == kApply || mirror) {
+      // The mirrored tile of the symmetric products (B' X keeps one layout).
+      if (mirror) {
         lds_transposed();
-        if (MODE == kApply)
-          store_rows(reinterpret_cast<uint8_t*>(pr.OT) + ((size_t)wcol0 * pr.ldot + wrow0) * sizeof(T), pr.ldot);
-        else
-          store_rows(reinterpret_cast<uint8_t*>(pr.O) + ((size_t)wcol0 * pr.ldo + wrow0) * sizeof(T), pr.ldo);
+        store_rows(reinterpret_cast<uint8_t*>(pr.O) + ((size_t)wcol0 * pr.ldo + wrow0) * sizeof(T), pr.ldo);
       }
     }
   } else {

@@ -44,6 +44,7 @@ int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 constexpr int64_t kMaxDim = 1 << 16;   // padded Newton-Schulz dims fit int32 tile math
 constexpr size_t kAlign = 256;
+constexpr size_t kNoBuffer = ~(size_t)0;   // workspace offset of a buffer the plan does not have
 
 struct MatPlan {
   int64_t rows, cols;
@@ -268,12 +269,15 @@ int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& op
   // Every Newton-Schulz buffer row is kRowSkewBytes longer than the padded
   // dim: with power-of-two pitches the 256 rows a tile streams at one K
   // offset would all land in the same L2 channel.
+  // The bf16 path keeps the iterate in one layout (the GEMM reads X^T out of
+  // X through transposing LDS reads); the fp32 path also stores X^T.
   const int64_t skew = kRowSkewBytes / (int64_t)P.tsize;
+  const bool dual = P.tsize == 4;
   for (auto& m : P.mats) {
     const size_t ldn = (size_t)(m.n_pad + skew), ldm = (size_t)(m.m_pad + skew);
     for (int k = 0; k < 2; ++k) {
       m.off_X[k] = take((size_t)m.m_pad * ldn * P.tsize);
-      m.off_XT[k] = take((size_t)m.n_pad * ldm * P.tsize);
+      m.off_XT[k] = dual ? take((size_t)m.n_pad * ldm * P.tsize) : kNoBuffer;
     }
     m.off_A = take((size_t)m.m_pad * ldm * P.tsize);
     m.off_B = take((size_t)m.m_pad * ldm * P.tsize);
@@ -504,7 +508,7 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
     g.ld_skew = (int32_t)(kRowSkewBytes / pl.tsize);
     for (int k = 0; k < 2; ++k) {
       g.X[k] = h->ws + m.off_X[k];
-      g.XT[k] = h->ws + m.off_XT[k];
+      g.XT[k] = m.off_XT[k] == kNoBuffer ? nullptr : h->ws + m.off_XT[k];
     }
     g.U = h->ws + m.off_U;
     g.mom_tile0 = m.mom_tile0;
@@ -528,7 +532,7 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
       GemmProb& c = apply[k][i];
       std::memset(&c, 0, sizeof(c));
       c.P = h->ws + m.off_B;
-      c.Q = g.XT[k];
+      c.Q = g.XT[k] ? g.XT[k] : g.X[k];   // bf16: X itself, read K-major
       c.E = nullptr;
       c.O = g.X[k ^ 1];
       c.OT = g.XT[k ^ 1];
@@ -537,7 +541,7 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
       c.N = N;
       c.K = M;
       c.ldp = LM;
-      c.ldq = LM;
+      c.ldq = g.XT[k] ? LM : LN;
       c.lde = LM;
       c.ldo = LN;
       c.ldot = LM;
