@@ -186,6 +186,18 @@ double muonh_lr_power(double k, double peak, double floor_, double warmup,
  * steps (the §3.3.2 sweeps; plain reading of the pages).                     */
 double muonh_lr_wsd(double k, double peak, double total, double decay_ratio,
                     double warmup, double eta_min);
+/* Eq. (11) frozen from s_hold on: the constant-LR continuation that feeds
+ * checkpoint averaging (§3.4: held from step 218,000 at base LR 4.08e-5).
+ * Returns muonh_lr_linear(eta0, eta_min, min(s, s_hold), S).                */
+double muonh_lr_linear_hold(double eta0, double eta_min, double s, double S, double s_hold);
+/* Cosine decay from eta_max to eta_min over `total` steps after a linear
+ * warmup of `warmup` steps (the post-training schedule, App. E); k is
+ * clamped to [warmup, total] for the decay part.                            */
+double muonh_lr_cosine(double k, double total, double eta_max, double eta_min, double warmup);
+/* Effective LR of a Hyperball-wrapped matrix from the base schedule:
+ * eta^H = multiplier * eta_base (§3.3.1; multiplier 10 in App. C, Tab. 8).
+ * This is the value muonh_step_args.elr takes.                              */
+double muonh_elr_from_base(double eta_base, double multiplier);
 
 #ifdef __cplusplus
 }

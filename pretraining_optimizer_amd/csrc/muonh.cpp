@@ -813,4 +813,17 @@ double muonh_lr_wsd(double k, double peak, double total, double decay_ratio, dou
   return muonh_lr_linear(peak, eta_min, k - d0, total - d0);
 }
 
+double muonh_lr_linear_hold(double eta0, double eta_min, double s, double S, double s_hold) {
+  return muonh_lr_linear(eta0, eta_min, std::min(s, s_hold), S);
+}
+
+double muonh_lr_cosine(double k, double total, double eta_max, double eta_min, double warmup) {
+  if (warmup > 0.0 && k < warmup) return eta_max * k / warmup;
+  const double span = std::max(total - warmup, 1.0);
+  const double t = std::min(std::max((k - warmup) / span, 0.0), 1.0);
+  return eta_min + 0.5 * (eta_max - eta_min) * (1.0 + std::cos(M_PI * t));
+}
+
+double muonh_elr_from_base(double eta_base, double multiplier) { return multiplier * eta_base; }
+
 }  // extern "C"

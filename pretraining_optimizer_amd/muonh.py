@@ -98,6 +98,9 @@ _SIGNATURES = [
     ("muonh_lr_linear", ctypes.c_double, [ctypes.c_double] * 4),
     ("muonh_lr_power", ctypes.c_double, [ctypes.c_double] * 6),
     ("muonh_lr_wsd", ctypes.c_double, [ctypes.c_double] * 6),
+    ("muonh_lr_linear_hold", ctypes.c_double, [ctypes.c_double] * 5),
+    ("muonh_lr_cosine", ctypes.c_double, [ctypes.c_double] * 5),
+    ("muonh_elr_from_base", ctypes.c_double, [ctypes.c_double] * 2),
 ]
 
 

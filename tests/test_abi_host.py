@@ -3,6 +3,7 @@ point the header declares, plans and validates without a device, and its
 LR helpers agree with the oracle's schedules."""
 
 import ctypes
+import json
 import os
 import re
 
@@ -123,3 +124,31 @@ def test_lr_helpers_match_oracle_schedules():
     for k in (0, 2, 5, 7.5, 10):
         assert lib.muonh_lr_wsd(k, 0.024, 10.0, 0.5, 0.0, 0.0) == pytest.approx(
             oracle.lr_wsd(k, 0.024, 10, 0.5), rel=1e-14, abs=1e-18)
+
+
+def test_hold_cosine_and_multiplier_helpers():
+    lib = pm.load_library()
+    sched = lambda s: oracle.lr_linear(1.04e-3, 1e-5, s, 500.0)
+    for s in (0.0, 100.0, 300.0, 301.0, 450.0, 600.0):
+        assert lib.muonh_lr_linear_hold(1.04e-3, 1e-5, s, 500.0, 300.0) == pytest.approx(
+            oracle.lr_constant_hold(s, 300.0, sched), rel=1e-15)
+    for k in (0.0, 5.0, 10.0, 37.0, 50.0, 99.0, 100.0, 150.0):
+        assert lib.muonh_lr_cosine(k, 100.0, 1e-5, 1e-7, 10.0) == pytest.approx(
+            oracle.lr_cosine(k, 100.0, 1e-5, 1e-7, warmup=10.0), rel=1e-14)
+    assert lib.muonh_elr_from_base(1.04e-3, 10.0) == pytest.approx(oracle.hyperball_lr(1.04e-3))
+
+
+def test_cma_hold_value_printed_on_the_pages():
+    """The held LR of the constant-LR continuation, through the C helpers:
+    Phase-1 end of Eq. (10), then Eq. (11) frozen at the hold step."""
+    pins = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "schedule_pins.json")))
+    lib = pm.load_library()
+    tps = pins["tokens_per_step"]
+    eta0 = lib.muonh_lr_power(pins["phase1_end"]["tokens"] / tps, 5e-3, 5e-4, 1000.0, 1000.0, 0.5)
+    h = pins["cma_hold"]
+    S = h["run_last_step"] - h["phase2_start_step"]
+    for k in (h["hold_step"], 220000, h["run_last_step"]):
+        v = lib.muonh_lr_linear_hold(eta0, h["eta_min"], k - h["phase2_start_step"], S,
+                                     h["hold_step"] - h["phase2_start_step"])
+        assert float(f"{v:.3g}") == h["printed_base_lr"]
+        assert float(f"{lib.muonh_elr_from_base(v, 10.0):.3g}") == h["printed_hyperball_lr"]
