@@ -59,6 +59,16 @@ def qwen3_layer_shapes(d_model: int, d_ff: int, n_q: int = 16, n_kv: int = 8,
     ]
 
 
+def qwen3_fused_layer_shapes(d_model: int, d_ff: int, n_q: int = 16, n_kv: int = 8,
+                             head: int = 128) -> List[Tuple[str, Shape]]:
+    """The same layer with the projections that share an input fused into
+    one matrix each: qkv = [q; k; v] and gate_up = [gate; up]."""
+    q = n_q * head
+    kv = n_kv * head
+    return [("qkv", (q + 2 * kv, d_model)), ("o", (d_model, q)),
+            ("gate_up", (2 * d_ff, d_model)), ("down", (d_model, d_ff))]
+
+
 def diag170m_layer_shapes() -> List[Tuple[str, Shape]]:
     return [("q", (768, 768)), ("k", (768, 768)), ("v", (768, 768)), ("o", (768, 768)),
             ("gate", (2048, 768)), ("up", (2048, 768)), ("down", (768, 2048))]
@@ -123,7 +133,7 @@ def _phase2_start(k: int) -> float:
 
 
 def workload(name: str) -> Workload:
-    """The five synthetic workloads (shapes, dtypes, steps and LR)."""
+    """The synthetic workloads (shapes, dtypes, steps and LR)."""
     if name == "single":
         return Workload("single", [("w", (256, 128))], torch.float32, "f32", 3, 0.95,
                         lambda k: 0.01, w_std=0.02)
@@ -138,13 +148,16 @@ def workload(name: str) -> Workload:
     if name == "qwen3_1.7b":
         mats = [(f"l{l}.{n}", s) for l in range(28) for n, s in qwen3_layer_shapes(2048, 6144)]
         return Workload("qwen3_1.7b", mats, torch.bfloat16, "bf16", 10, 0.95, _phase2_start)
+    if name == "qwen3_1.7b_fused":
+        mats = [(f"l{l}.{n}", s) for l in range(28) for n, s in qwen3_fused_layer_shapes(2048, 6144)]
+        return Workload("qwen3_1.7b_fused", mats, torch.bfloat16, "bf16", 10, 0.95, _phase2_start)
     if name == "stress":
         return Workload("stress", stress_shapes(0), torch.float32, "f32", 3, 0.95,
                         lambda k: 0.02, grad_kind="lowrank")
     raise KeyError(name)
 
 
-WORKLOADS = ("single", "diag170m", "qwen3_0.6b", "qwen3_1.7b", "stress")
+WORKLOADS = ("single", "diag170m", "qwen3_0.6b", "qwen3_1.7b", "qwen3_1.7b_fused", "stress")
 
 
 # ---------------------------------------------------------------------------

@@ -108,6 +108,20 @@ def test_qwen3_17b_full_size():
         assert len(rep.norm_err) == 196
 
 
+def test_qwen3_17b_fused_projections():
+    """Qwen3-1.7B dims with fused qkv (4096 x 2048) and gate_up (12288 x 2048)
+    matrices: wider Newton-Schulz problems (n up to 12288) in the same grouped
+    launches; the oracle checks the four matrices of layer 0."""
+    announce("qwen3-1.7b fused projections, 1 step")
+    wl = inputs.workload("qwen3_1.7b_fused")
+    mw, mg = workload_fns(wl)
+    etas = [wl.eta(0)]
+    reps = run_parity(wl.shapes, mw, mg, etas, check=list(range(4)), ns="bf16")
+    check_reports(reps, TOL_BF16, etas)
+    for rep in reps:
+        assert len(rep.norm_err) == 112
+
+
 def test_stats_match_oracle_diagnostics():
     announce("stats vs oracle diagnostics")
     shapes = [(256, 512), (700, 300)]

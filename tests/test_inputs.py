@@ -17,6 +17,14 @@ def test_workload_param_counts():
     assert w.params() == 28 * (2 * 2048 * 2048 + 2 * 1024 * 2048 + 3 * 6144 * 2048)
 
 
+def test_fused_workload_has_the_split_parameters():
+    split = inputs.workload("qwen3_1.7b")
+    fused = inputs.workload("qwen3_1.7b_fused")
+    assert len(fused.shapes) == 28 * 4
+    assert fused.params() == split.params()
+    assert fused.shapes[:4] == [(4096, 2048), (2048, 2048), (12288, 2048), (2048, 6144)]
+
+
 def test_stress_shapes():
     shapes = inputs.workload("stress").shapes
     assert len(shapes) == 64
