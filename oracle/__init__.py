@@ -1,4 +1,5 @@
-"""CPU fp64 oracle for the MuonH optimizer step.
+"""CPU fp64 oracle for the MuonH optimizer step and the AdamW step of the
+parameters MuonH does not wrap.
 
 TEST INFRASTRUCTURE ONLY.  This package is the plain, slow, obviously-correct
 statement of what the GPU library computes.  Only the tests, the smoke check
@@ -44,4 +45,12 @@ from .schedules import (  # noqa: F401
     lr_constant_hold,
     lr_cosine,
     hyperball_lr,
+)
+from .adamw import (  # noqa: F401
+    AdamWOptions,
+    adamw_step,
+    adamw_trajectory,
+    adamw_bytes_per_element,
+    first_step_direction,
+    constant_gradient_closed_form,
 )
