@@ -6,7 +6,9 @@ iterations on the grouped MFMA GEMM engine, reductions, Hyperball update)
 over every matrix of the workload, with weights, momenta and gradients
 resident in HBM.  Default workload: the 196 Qwen3-1.7B-shaped matrices
 (28 layers x q, k, v, o, gate, up, down), fp32 W and M, bf16 gradients,
-bf16 Newton-Schulz operands with fp32 accumulation.
+bf16 Newton-Schulz operands with fp32 accumulation.  The AdamW step of the
+parameters MuonH does not wrap (embedding, LM head, normalisation weights of
+the untied Qwen3-1.7B model) is timed separately and reported beside it.
 
 Prints ONE JSON line on stdout; a human-readable breakdown goes to stderr.
 
@@ -130,6 +132,39 @@ def cpu_baseline(wl, ws_dev, grads_dev, eta, layer_mats: int):
             "seconds_sample": dt, "host_cpus": os.cpu_count()}
 
 
+def time_adamw(steps: int, warmup: int, dev):
+    """The AdamW step of the parameters MuonH does not wrap (untied Qwen3-1.7B
+    embedding, LM head and normalisation weights), timed with HIP events on
+    the stream it is launched on."""
+    import torch
+    import inputs
+    import pretraining_optimizer_amd as pm
+    grp = inputs.adamw_group("qwen3_1.7b")
+    n = len(grp.tensors)
+    ws = [inputs.make_adamw_param(grp, i, dev) for i in range(n)]
+    ms = [torch.zeros_like(w) for w in ws]
+    vs = [torch.zeros_like(w) for w in ws]
+    gs = [inputs.make_adamw_grad(grp, 0, i, dev) for i in range(n)]
+    opt = pm.AdamW(ws, ms, vs, grad_dtype=grp.g_dtype)
+    for k in range(warmup):
+        opt.step(gs, grp.lr(k), k + 1)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for k in range(steps):
+        opt.step(gs, grp.lr(warmup + k), warmup + k + 1)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    opt.close()
+    gsize = 2 if grp.g_dtype == torch.bfloat16 else 4
+    nbytes = grp.params() * (gsize + 24)   # g in; W, m, v (fp32) in and out
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    log(f"adamw group: {grp.params() / 1e9:.3f} G params, {ms_step:.3f} ms/step, {gbs:.0f} GB/s")
+    return {"params": grp.params(), "tensors": n, "ms": ms_step, "bytes_per_step": nbytes,
+            "gbs": gbs, "frac_of_hbm": gbs / PEAK_HBM_GBS}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +176,8 @@ def main():
     ap.add_argument("--cpu-mats", type=int, default=7,
                     help="matrices the CPU oracle times (default: one layer)")
     ap.add_argument("--grad-sets", type=int, default=4)
+    ap.add_argument("--no-adamw", action="store_true",
+                    help="skip timing the AdamW step of the non-MuonH parameters")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="also run one plain device-to-device copy of BYTES (for counter calibration)")
     args = ap.parse_args()
@@ -254,6 +291,8 @@ def main():
             "kernel": names[dom], "flop_per_launch": fl[dom] / launches[dom],
             "ms_per_launch": kern[dom]["ms_per_launch"]}
 
+    adamw = None if args.no_adamw else time_adamw(args.steps, args.warmup, dev)
+
     cpu = None
     if cpu_inputs is not None:
         log(f"cpu baseline: oracle on {args.cpu_mats} matrices ...")
@@ -276,6 +315,7 @@ def main():
         "elementwise_alg18_gbs": alg_gbs,
         "kernels": kern, "phase_ms_per_step": per_step, "timed_steps_events": nt,
         "norm_invariant_max_dev": norm_dev,
+        "adamw_group": adamw,
         "cpu_baseline": cpu,
     }
     opt.close()

@@ -199,6 +199,58 @@ double muonh_lr_cosine(double k, double total, double eta_max, double eta_min, d
  * This is the value muonh_step_args.elr takes.                              */
 double muonh_elr_from_base(double eta_base, double multiplier);
 
+/* ---- AdamW for the parameters MuonH does not wrap -----------------------
+ * The pages train embeddings, normalisation layers, the LM head and every
+ * other non-wrapped parameter with AdamW at weight decay 0.1 on the base LR
+ * schedule (§3.3; App. C, Tab. 8), and use Adam betas (0.9, 0.95) and
+ * epsilon 1e-12 (App. E).  The update rule is the standard decoupled-decay
+ * AdamW with bias correction, for step count t = 1, 2, ... and LR lr:
+ *     W <- W (1 - lr wd);  m <- b1 m + (1-b1) g;  v <- b2 v + (1-b2) g^2
+ *     W <- W - lr (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps)
+ * computed in fp32 per element, one multi-tensor launch per step.
+ * Conventions are those listed at the top of this file.                     */
+typedef struct muonh_adamw_handle muonh_adamw_handle;
+
+typedef struct muonh_adamw_tensor {
+  void* w;          /* fp32 parameter, device, contiguous, updated in place    */
+  const void* g;    /* gradient, device, g_dtype                                */
+  void* m;          /* fp32 first moment, device, in place (zeros before t = 1) */
+  void* v;          /* fp32 second moment, device, in place (zeros before t = 1)*/
+  int64_t numel;    /* elements, >= 1                                           */
+  int32_t g_dtype;  /* MUONH_F32 or MUONH_BF16                                  */
+  int32_t reserved; /* must be 0                                                */
+} muonh_adamw_tensor;
+
+typedef struct muonh_adamw_options {
+  float beta1;         /* 0.9  */
+  float beta2;         /* 0.95 */
+  float eps;           /* 1e-12 */
+  float weight_decay;  /* 0.1  */
+} muonh_adamw_options;
+
+/* Fill *opt with the defaults listed above. */
+void muonh_adamw_default_options(muonh_adamw_options* opt);
+
+/* Plan the chunk table for these tensors (sizes and gradient dtypes are kept,
+ * pointers are not) and allocate its small device tables on the current
+ * device.  Errors: MUONH_EINVAL for n < 1, numel < 1, an unknown dtype, a
+ * nonzero reserved field or options outside 0 <= beta < 1, eps > 0,
+ * weight_decay >= 0; MUONH_EHIP for a HIP failure.  On failure *h is NULL. */
+int muonh_adamw_init(muonh_adamw_handle** h, const muonh_adamw_tensor* t, int32_t n,
+                     const muonh_adamw_options* opt);
+
+/* One AdamW step at step count `step` (>= 1) with learning rate `lr` over the
+ * same list (order, sizes, dtypes) as init; pointers may change between
+ * steps.  w, m, v and an fp32 g must be 16-byte aligned, a bf16 g 8-byte
+ * aligned.  Asynchronous on `stream`.  Errors: MUONH_EINVAL (null or
+ * misaligned pointer, step < 1, non-finite lr), MUONH_EMISMATCH (list
+ * differs from init), MUONH_EHIP.                                            */
+int muonh_adamw_step(muonh_adamw_handle* h, const muonh_adamw_tensor* t, int32_t n,
+                     float lr, int64_t step, void* stream);
+
+/* Release the handle (waits for its last upload).  NULL is a no-op. */
+int muonh_adamw_destroy(muonh_adamw_handle* h);
+
 #ifdef __cplusplus
 }
 #endif

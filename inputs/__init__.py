@@ -26,6 +26,7 @@ import torch
 Shape = Tuple[int, int]
 
 ROLE_W, ROLE_G = 1, 2
+ROLE_AW, ROLE_AG = 3, 4     # parameters / gradients of the AdamW group
 
 
 def stream_seed(seed: int, step: int, index: int, role: int) -> int:
@@ -210,3 +211,78 @@ def make_grads(wl: Workload, step: int, device="cpu", indices: Optional[Sequence
 def to_numpy64(t: torch.Tensor) -> np.ndarray:
     """Exact fp64 copy of a (possibly bf16) tensor, on the host."""
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+# ---------------------------------------------------------------------------
+# the AdamW parameter group (embeddings, normalisation layers, LM head)
+
+# Qwen3 tokenizer vocabulary.  The pages state only that the untied Qwen3-1.7B
+# architecture has about 2B parameters [arXiv §2]; with this vocabulary the
+# embedding and LM head add 2 x 151936 x 2048 = 0.62B to the 1.41B of the
+# MuonH matrices (2.03B in total).
+QWEN3_VOCAB = 151936
+
+
+@dataclasses.dataclass
+class AdamwGroup:
+    name: str
+    tensors: List[Tuple[str, int, str]]   # (name, numel, kind: "matrix" | "norm")
+    g_dtype: torch.dtype
+    steps: int
+    lr: Callable[[int], float]            # base LR at step k (0-based)
+    seed: int = 0
+
+    def numels(self) -> List[int]:
+        return [n for _, n, _ in self.tensors]
+
+    def params(self) -> int:
+        return sum(self.numels())
+
+
+def qwen3_adamw_tensors(d_model: int, layers: int = 28, head: int = 128,
+                        vocab: int = QWEN3_VOCAB) -> List[Tuple[str, int, str]]:
+    """Flat sizes of the parameters AdamW trains in the untied Qwen3
+    architecture: embedding and LM head [vocab x d_model]; per layer the two
+    RMSNorm weights and the q / k head norms; the final norm."""
+    out = [("embed", vocab * d_model, "matrix"), ("lm_head", vocab * d_model, "matrix")]
+    for l in range(layers):
+        out += [(f"l{l}.input_norm", d_model, "norm"), (f"l{l}.post_attn_norm", d_model, "norm"),
+                (f"l{l}.q_norm", head, "norm"), (f"l{l}.k_norm", head, "norm")]
+    out.append(("final_norm", d_model, "norm"))
+    return out
+
+
+def _phase2_base(k: int) -> float:
+    return _ETA0 + (1e-5 - _ETA0) * k / _S2
+
+
+RAGGED_ADAMW = [1, 3, 5, 1000, 4096, 16384, 16385, 70001, 6149]
+
+
+def adamw_group(name: str) -> AdamwGroup:
+    """'qwen3_1.7b': the AdamW group of the untied Qwen3-1.7B model at the
+    Phase-2 start of the base schedule; 'ragged_bf16' / 'ragged_f32': small
+    tensors with ragged sizes for element-by-element parity."""
+    if name == "qwen3_1.7b":
+        return AdamwGroup(name, qwen3_adamw_tensors(2048), torch.bfloat16, 10, _phase2_base)
+    if name in ("ragged_bf16", "ragged_f32"):
+        ts = [(f"t{i}", n, "norm" if i % 3 == 0 else "matrix") for i, n in enumerate(RAGGED_ADAMW)]
+        g = torch.bfloat16 if name == "ragged_bf16" else torch.float32
+        return AdamwGroup(name, ts, g, 4, lambda k: 3e-3 * (1.0 - k / 8.0), seed=7)
+    raise KeyError(name)
+
+
+def make_adamw_param(grp: AdamwGroup, index: int, device="cpu") -> torch.Tensor:
+    """Parameter `index` at step 0: N(0, 0.02^2) for matrices, 1 + N(0, 0.02^2)
+    for normalisation weights (fp32, flat)."""
+    _, n, kind = grp.tensors[index]
+    p = _randn((n,), stream_seed(grp.seed, 0, index, ROLE_AW), device) * 0.02
+    if kind == "norm":
+        p = p + 1.0
+    return p.contiguous()
+
+
+def make_adamw_grad(grp: AdamwGroup, step: int, index: int, device="cpu") -> torch.Tensor:
+    """Gradient of tensor `index` at step `step`: N(0, 1), stored in grp.g_dtype."""
+    _, n, _ = grp.tensors[index]
+    return _randn((n,), stream_seed(grp.seed, step, index, ROLE_AG), device).to(grp.g_dtype).contiguous()

@@ -3,12 +3,15 @@
 The library (libmuonh.so, built from csrc/ by ``build.py``) runs momentum,
 quintic Newton-Schulz on a grouped bf16/fp32 MFMA GEMM engine and the
 Hyperball update of Eq. (1) of "Puro-2B: Poor Lab's Qwen2-1.5B Trained on
-RTX 5090 within $5090" (arXiv HTML §3.3).  ``muonh`` is its ctypes binding.
+RTX 5090 within $5090" (arXiv HTML §3.3), plus the AdamW step of the
+parameters MuonH does not wrap.  ``muonh`` is its ctypes binding.
 """
 
 from .muonh import (  # noqa: F401
+    AdamW,
     MuonH,
     MuonHError,
+    adamw_default_options,
     default_options,
     load_library,
     plan_query,

@@ -359,6 +359,88 @@ __global__ __launch_bounds__(kElemThreads) void copy_update_kernel(const T* __re
   if constexpr (sizeof(T) == 2) dst[i] = bf16_to_f32(U[i]); else dst[i] = U[i];
 }
 
+// ---------------------------------------------------------------------------
+// AdamW (decoupled weight decay, bias-corrected), one chunk per block, fp32.
+
+__device__ __forceinline__ float adamw_elem(float w, float& m, float& v, float g,
+                                            const AdamwParams& p) {
+  m = p.beta1 * m + p.omb1 * g;
+  v = p.beta2 * v + p.omb2 * (g * g);
+  const float denom = sqrtf(v) * p.rbc2 + p.eps;
+  return w * p.decay - p.step_size * (m / denom);
+}
+
+__device__ __forceinline__ void adamw4(f32x4_t& w, f32x4_t& m, f32x4_t& v, const f32x4_t& g,
+                                       const AdamwParams& p) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float me = m[e], ve = v[e];
+    w[e] = adamw_elem(w[e], me, ve, g[e], p);
+    m[e] = me;
+    v[e] = ve;
+  }
+}
+
+template <typename G>
+__device__ __forceinline__ void adamw_chunk(const Chunk& c, const AdamwPtrs& q,
+                                            const AdamwParams& p) {
+  float* W = q.w + c.start;
+  float* Mm = q.m + c.start;
+  float* V = q.v + c.start;
+  const G* Gp = reinterpret_cast<const G*>(q.g) + c.start;
+  const int tid = threadIdx.x;
+  const int n4 = c.len & ~3;
+  constexpr int kStep = kElemThreads * 4;
+  // Batches of 2 x 4 elements per thread, every load issued before the
+  // stores (W, m, v are written in place).
+  int i = tid * 4;
+  for (; i + kStep < n4; i += 2 * kStep) {
+    f32x4_t w[2], m[2], v[2], g[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      w[k] = Vec4<float>::load(W + i + k * kStep);
+      m[k] = Vec4<float>::load(Mm + i + k * kStep);
+      v[k] = Vec4<float>::load(V + i + k * kStep);
+      g[k] = Vec4<G>::load(Gp + i + k * kStep);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      adamw4(w[k], m[k], v[k], g[k], p);
+      Vec4<float>::store(W + i + k * kStep, w[k]);
+      Vec4<float>::store(Mm + i + k * kStep, m[k]);
+      Vec4<float>::store(V + i + k * kStep, v[k]);
+    }
+  }
+  for (; i < n4; i += kStep) {
+    f32x4_t w = Vec4<float>::load(W + i), m = Vec4<float>::load(Mm + i);
+    f32x4_t v = Vec4<float>::load(V + i);
+    const f32x4_t g = Vec4<G>::load(Gp + i);
+    adamw4(w, m, v, g, p);
+    Vec4<float>::store(W + i, w);
+    Vec4<float>::store(Mm + i, m);
+    Vec4<float>::store(V + i, v);
+  }
+  for (int j = n4 + tid; j < c.len; j += kElemThreads) {
+    float g;
+    if constexpr (sizeof(G) == 2) g = bf16_to_f32(Gp[j]); else g = Gp[j];
+    float m = Mm[j], v = V[j];
+    W[j] = adamw_elem(W[j], m, v, g, p);
+    Mm[j] = m;
+    V[j] = v;
+  }
+}
+
+__global__ __launch_bounds__(kElemThreads) void adamw_kernel(const Chunk* __restrict__ chunks,
+                                                             const AdamwPtrs* __restrict__ ptrs,
+                                                             AdamwParams prm) {
+  const Chunk c = chunks[blockIdx.x];
+  const AdamwPtrs q = ptrs[c.mat];
+  if (q.g_bf16)
+    adamw_chunk<uint16_t>(c, q, prm);
+  else
+    adamw_chunk<float>(c, q, prm);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -438,6 +520,14 @@ hipError_t launch_copy_update(int bf16, const void* U, int64_t count, float* dst
   else
     hipLaunchKernelGGL(copy_update_kernel<float>, dim3(grid), dim3(kElemThreads), 0, st,
                        reinterpret_cast<const float*>(U), count, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw(const Chunk* chunks, int64_t nchunks, const AdamwPtrs* ptrs,
+                        AdamwParams prm, hipStream_t st) {
+  if (nchunks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)nchunks), dim3(kElemThreads), 0, st, chunks,
+                     ptrs, prm);
   return hipGetLastError();
 }
 

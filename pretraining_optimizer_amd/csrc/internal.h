@@ -137,4 +137,27 @@ hipError_t launch_finalize_radius(int32_t nmat, const MatGeom* geo, const double
 
 hipError_t launch_copy_update(int bf16, const void* U, int64_t count, float* dst, hipStream_t st);
 
+// AdamW over a list of flat tensors (chunks of kChunk elements).
+struct AdamwPtrs {
+  float* w;
+  const void* g;
+  float* m;
+  float* v;
+  int32_t g_bf16;
+  int32_t pad;
+};
+struct AdamwParams {
+  float beta1, omb1;    // beta1, 1 - beta1
+  float beta2, omb2;    // beta2, 1 - beta2
+  float eps;
+  float decay;          // 1 - lr * weight_decay
+  float step_size;      // lr / (1 - beta1^t)
+  float rbc2;           // 1 / sqrt(1 - beta2^t)
+};
+hipError_t launch_adamw(const Chunk* chunks, int64_t nchunks, const AdamwPtrs* ptrs,
+                        AdamwParams prm, hipStream_t st);
+
+// Records the text of a failure for muonh_last_error() and returns `code`.
+int set_last_error(int code, const char* msg);
+
 }  // namespace muonh

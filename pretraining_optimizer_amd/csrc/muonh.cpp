@@ -24,8 +24,15 @@
 using namespace muonh;
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
+
+int muonh::set_last_error(int code, const char* msg) {
+  g_last_error = msg;
+  return code;
+}
+
+namespace {
 
 int fail(int code, const std::string& msg) {
   g_last_error = msg;

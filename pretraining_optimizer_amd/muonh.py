@@ -54,6 +54,17 @@ class muonh_step_args(ctypes.Structure):
                 ("step", ctypes.c_int64), ("want_stats", ctypes.c_int32)]
 
 
+class muonh_adamw_tensor(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("g", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("numel", ctypes.c_int64), ("g_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class muonh_adamw_options(ctypes.Structure):
+    _fields_ = [("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
+                ("weight_decay", ctypes.c_float)]
+
+
 class muonh_stats(ctypes.Structure):
     _fields_ = [("y_norm", ctypes.c_double), ("u_norm", ctypes.c_double),
                 ("w_norm", ctypes.c_double), ("inner", ctypes.c_double), ("c", ctypes.c_double),
@@ -101,6 +112,12 @@ _SIGNATURES = [
     ("muonh_lr_linear_hold", ctypes.c_double, [ctypes.c_double] * 5),
     ("muonh_lr_cosine", ctypes.c_double, [ctypes.c_double] * 5),
     ("muonh_elr_from_base", ctypes.c_double, [ctypes.c_double] * 2),
+    ("muonh_adamw_default_options", None, [ctypes.POINTER(muonh_adamw_options)]),
+    ("muonh_adamw_init", ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(muonh_adamw_tensor),
+                                        ctypes.c_int32, ctypes.POINTER(muonh_adamw_options)]),
+    ("muonh_adamw_step", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(muonh_adamw_tensor), ctypes.c_int32,
+                                        ctypes.c_float, ctypes.c_int64, ctypes.c_void_p]),
+    ("muonh_adamw_destroy", ctypes.c_int, [ctypes.c_void_p]),
 ]
 
 
@@ -285,6 +302,82 @@ class MuonH:
     def close(self):
         if getattr(self, "_h", None):
             self._lib.muonh_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def adamw_default_options(**overrides) -> muonh_adamw_options:
+    opt = muonh_adamw_options()
+    load_library().muonh_adamw_default_options(ctypes.byref(opt))
+    for k, v in overrides.items():
+        if not hasattr(opt, k):
+            raise KeyError(f"unknown AdamW option {k}")
+        setattr(opt, k, v)
+    return opt
+
+
+class AdamW:
+    """AdamW over a list of fp32 CUDA tensors (parameters, first and second
+    moments updated in place), one multi-tensor launch per step.
+
+    params, exp_avgs, exp_avg_sqs : lists of contiguous fp32 CUDA tensors
+    grad_dtype                    : torch dtype of the gradients passed to step()
+    options                       : beta1, beta2, eps, weight_decay overrides
+    """
+
+    def __init__(self, params: List, exp_avgs: List, exp_avg_sqs: List, grad_dtype=None,
+                 **options):
+        import torch
+        self._lib = load_library()
+        if not params or not (len(params) == len(exp_avgs) == len(exp_avg_sqs)):
+            raise ValueError("params, exp_avgs and exp_avg_sqs must be non-empty lists of equal length")
+        grad_dtype = torch.bfloat16 if grad_dtype is None else grad_dtype
+        for p, m, v in zip(params, exp_avgs, exp_avg_sqs):
+            for t in (p, m, v):
+                if not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous():
+                    raise ValueError("params and moments must be contiguous fp32 CUDA tensors")
+            if p.numel() != m.numel() or p.numel() != v.numel():
+                raise ValueError("a parameter and its moments must have the same size")
+        self.n = len(params)
+        self.params, self.exp_avgs, self.exp_avg_sqs = list(params), list(exp_avgs), list(exp_avg_sqs)
+        self.numels = [p.numel() for p in params]
+        self._gcode = {torch.bfloat16: MUONH_BF16, torch.float32: MUONH_F32}[grad_dtype]
+        self.options = adamw_default_options(**options)
+        d = (muonh_adamw_tensor * self.n)()
+        for i in range(self.n):
+            d[i].numel = self.numels[i]
+            d[i].g_dtype = self._gcode
+        h = ctypes.c_void_p()
+        _check(self._lib.muonh_adamw_init(ctypes.byref(h), d, self.n, ctypes.byref(self.options)),
+               "muonh_adamw_init")
+        self._h = h
+        self._d = d
+
+    def step(self, grads: Sequence, lr: float, step: int, stream=None):
+        """One step at step count `step` (1-based) with learning rate `lr`."""
+        if len(grads) != self.n:
+            raise ValueError("one gradient per tensor is required")
+        d = self._d
+        for i, g in enumerate(grads):
+            if not g.is_cuda or not g.is_contiguous() or g.numel() != self.numels[i]:
+                raise ValueError(f"gradient {i}: must be a contiguous CUDA tensor of {self.numels[i]} elements")
+            if _dtype_code(g) != self._gcode:
+                raise TypeError(f"gradient {i}: dtype differs from the one given at init")
+            d[i].w = self.params[i].data_ptr()
+            d[i].g = g.data_ptr()
+            d[i].m = self.exp_avgs[i].data_ptr()
+            d[i].v = self.exp_avg_sqs[i].data_ptr()
+        _check(self._lib.muonh_adamw_step(self._h, d, self.n, float(lr), int(step), _stream_ptr(stream)),
+               "muonh_adamw_step")
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.muonh_adamw_destroy(self._h)
             self._h = None
 
     def __del__(self):

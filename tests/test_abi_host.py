@@ -152,3 +152,35 @@ def test_cma_hold_value_printed_on_the_pages():
                                      h["hold_step"] - h["phase2_start_step"])
         assert float(f"{v:.3g}") == h["printed_base_lr"]
         assert float(f"{lib.muonh_elr_from_base(v, 10.0):.3g}") == h["printed_hyperball_lr"]
+
+
+def test_adamw_defaults_and_host_validation():
+    lib = pm.load_library()
+    o = mb.muonh_adamw_options()
+    lib.muonh_adamw_default_options(ctypes.byref(o))
+    assert (o.beta1, o.beta2, o.weight_decay) == pytest.approx((0.9, 0.95, 0.1))
+    assert o.eps == pytest.approx(1e-12)
+    h = ctypes.c_void_p()
+    t = (mb.muonh_adamw_tensor * 2)()
+    for i in range(2):
+        t[i].numel, t[i].g_dtype = 1000, mb.MUONH_BF16
+    assert lib.muonh_adamw_init(None, t, 2, None) == mb.MUONH_EINVAL
+    assert lib.muonh_adamw_init(ctypes.byref(h), None, 2, None) == mb.MUONH_EINVAL
+    assert lib.muonh_adamw_init(ctypes.byref(h), t, 0, None) == mb.MUONH_EINVAL
+    t[1].numel = 0
+    assert lib.muonh_adamw_init(ctypes.byref(h), t, 2, None) == mb.MUONH_EINVAL
+    t[1].numel, t[1].g_dtype = 5, 7
+    assert lib.muonh_adamw_init(ctypes.byref(h), t, 2, None) == mb.MUONH_EINVAL
+    t[1].g_dtype, t[1].reserved = mb.MUONH_F32, 1
+    assert lib.muonh_adamw_init(ctypes.byref(h), t, 2, None) == mb.MUONH_EINVAL
+    t[1].reserved = 0
+    for bad in (dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0), dict(weight_decay=-1.0)):
+        ob = mb.muonh_adamw_options()
+        lib.muonh_adamw_default_options(ctypes.byref(ob))
+        for k, v in bad.items():
+            setattr(ob, k, v)
+        assert lib.muonh_adamw_init(ctypes.byref(h), t, 2, ctypes.byref(ob)) == mb.MUONH_EINVAL
+        assert lib.muonh_last_error()
+    assert not h.value
+    assert lib.muonh_adamw_step(None, t, 2, 1e-3, 1, None) == mb.MUONH_EINVAL
+    assert lib.muonh_adamw_destroy(None) == mb.MUONH_OK

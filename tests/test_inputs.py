@@ -62,3 +62,16 @@ def test_lowrank_grad_spectrum():
     s = np.linalg.svd(g, compute_uv=False)
     noise = math.sqrt(1e-3) * (math.sqrt(g.shape[0]) + math.sqrt(g.shape[1]))
     assert s[8] <= 1.2 * noise
+
+
+def test_adamw_group_sizes():
+    g = inputs.adamw_group("qwen3_1.7b")
+    assert g.params() == 2 * 151936 * 2048 + 28 * (2 * 2048 + 2 * 128) + 2048
+    total = g.params() + inputs.workload("qwen3_1.7b").params()
+    assert 1.95e9 < total < 2.1e9          # "about 2B parameters", untied
+    r = inputs.adamw_group("ragged_f32")
+    p = inputs.make_adamw_param(r, 0)
+    assert p.dtype == torch.float32 and p.numel() == r.numels()[0]
+    assert inputs.make_adamw_grad(r, 1, 3).dtype == torch.float32
+    assert torch.equal(inputs.make_adamw_grad(r, 1, 3), inputs.make_adamw_grad(r, 1, 3))
+    assert not torch.equal(inputs.make_adamw_grad(r, 1, 3), inputs.make_adamw_grad(r, 2, 3))
