@@ -217,7 +217,7 @@ def to_numpy64(t: torch.Tensor) -> np.ndarray:
 # the AdamW parameter group (embeddings, normalisation layers, LM head)
 
 # Qwen3 tokenizer vocabulary.  The pages state only that the untied Qwen3-1.7B
-# architecture has about 2B parameters [arXiv §2]; with this vocabulary the
+# architecture has about 2B parameters [arXiv §2.1]; with this vocabulary the
 # embedding and LM head add 2 x 151936 x 2048 = 0.62B to the 1.41B of the
 # MuonH matrices (2.03B in total).
 QWEN3_VOCAB = 151936
