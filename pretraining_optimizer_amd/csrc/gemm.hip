@@ -95,6 +95,10 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("" ::: "memory");
 }
 
+// Buffer descriptor word 3 for raw (unformatted, unswizzled) buffer access on
+// gfx9-family devices.
+constexpr int kBufferConfig = 0x00020000;
+
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100, kSgDsWrite = 0x200;
 #define MUONH_SG(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
@@ -214,28 +218,45 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   constexpr int kLd = kOperandBytes / 16 / kGemmThreads;   // 8 loads per operand
   const int srow = tid >> 3, schunk = tid & 7;
   const int qrow = tid >> 5, qchunk = tid & 31;
-  const uint8_t* pg = reinterpret_cast<const uint8_t*>(pr.P) + (size_t)(row0 + srow) * pstride + schunk * 16;
-  const uint8_t* qg = kQT ? reinterpret_cast<const uint8_t*>(pr.Q) + (size_t)qrow * qstride +
-                                (size_t)col0 * sizeof(T) + qchunk * 16
-                          : reinterpret_cast<const uint8_t*>(pr.Q) + (size_t)(col0 + srow) * qstride + schunk * 16;
+  // Operand loads are buffer loads: a uniform base (the tile's panel) in the
+  // descriptor, a per-thread byte offset fixed for the whole tile and a
+  // uniform per-load offset, so no vector address arithmetic is issued
+  // between the MFMAs.  Offsets stay below 2^31 (a panel spans < 32 MiB).
+  const uint8_t* pbase = reinterpret_cast<const uint8_t*>(pr.P) + (size_t)row0 * pstride;
+  const uint8_t* qbase = kQT ? reinterpret_cast<const uint8_t*>(pr.Q) + (size_t)col0 * sizeof(T)
+                             : reinterpret_cast<const uint8_t*>(pr.Q) + (size_t)col0 * qstride;
+  const __amdgpu_buffer_rsrc_t prs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pbase), (short)0, -1, kBufferConfig);
+  const __amdgpu_buffer_rsrc_t qrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(qbase), (short)0, -1, kBufferConfig);
+  const int pvoff = (int)(srow * pstride) + schunk * 16;
+  const int qvoff = kQT ? (int)(qrow * qstride) + qchunk * 16 : (int)(srow * qstride) + schunk * 16;
   const int sst = srow * kRowBytes + ((schunk ^ swz128(srow & 15)) << 4);
   const int sstq = kQT ? qrow * kTrPitch + ((qchunk ^ swz_tr(qrow)) << 4) : sst;
+  // s_waitcnt lgkmcnt(0) alone: this wavefront's LDS accesses are done.
+  auto wait_lds = [&]() {
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+    asm volatile("" ::: "memory");
+  };
   u32x4_t ra0[kLd], rb0[kLd], ra1[kLd], rb1[kLd];
   // Stages past the last one (the pipeline's tail) reload the last stage.
+  auto bload = [&](__amdgpu_buffer_rsrc_t rs, int voff, size_t soff) {
+    return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)soff, 0));
+  };
   auto gload_p = [&](u32x4_t (&r)[kLd], int kt) {
     const size_t koff = (size_t)min(kt, nk - 1) * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < kLd; ++i) r[i] = ld_global<u32x4_t>(pg + (size_t)(i * 32) * pstride + koff);
+    for (int i = 0; i < kLd; ++i) r[i] = bload(prs, pvoff, (size_t)(i * 32) * pstride + koff);
   };
   auto gload_q = [&](u32x4_t (&r)[kLd], int kt) {
     if constexpr (kQT) {
       const size_t k0 = (size_t)min(kt, nk - 1) * kTrRows;
 #pragma unroll
-      for (int i = 0; i < kLd; ++i) r[i] = ld_global<u32x4_t>(qg + (k0 + i * 8) * qstride);
+      for (int i = 0; i < kLd; ++i) r[i] = bload(qrs, qvoff, (k0 + i * 8) * qstride);
     } else {
       const size_t koff = (size_t)min(kt, nk - 1) * kRowBytes;
 #pragma unroll
-      for (int i = 0; i < kLd; ++i) r[i] = ld_global<u32x4_t>(qg + (size_t)(i * 32) * qstride + koff);
+      for (int i = 0; i < kLd; ++i) r[i] = bload(qrs, qvoff, (size_t)(i * 32) * qstride + koff);
     }
   };
   // Row i of this thread's share sits 4 KiB further in either Q layout.
@@ -243,11 +264,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     uint8_t* st = smem + slot * kStageBytes + operand * kOperandBytes + (operand ? sstq : sst);
 #pragma unroll
     for (int i = 0; i < kLd; ++i) *reinterpret_cast<u32x4_t*>(st + i * 4096) = r[i];
-  };
-  // s_waitcnt lgkmcnt(0) alone: this wavefront's LDS accesses are done.
-  auto wait_lds = [&]() {
-    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
-    asm volatile("" ::: "memory");
   };
   // One K stage read from LDS slot `cur`; register set (ra, rb) holds the
   // next stage, which goes to slot `nxt`, and is then refilled with stage
@@ -386,6 +402,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
       }
       wait_vmcnt<0>();   // this wavefront's region only: no barrier needed
     }
+    // (alpha is 1 except on the first iteration: skip the pass then)
+    if (MODE == kPoly || first_iter) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -420,6 +438,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
           acc[i][j][4 * g + 2] = v[2];
           acc[i][j][4 * g + 3] = v[3];
         }
+    }
     // The sub-tile goes to LDS row-major (2-byte writes, 4 per register group)
     // or transposed (one 8-byte write per register group), then leaves as
     // rows of 256 B.  LDS operations of one wavefront complete in issue
@@ -450,12 +469,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
           }
     };
     // LDS row rr -> dst + rr * ld (elements); whole, aligned 256-B rows.
+    // Eight LDS reads are in flight before their stores.
     auto store_rows = [&](uint8_t* dst, size_t ld) {
 #pragma unroll
-      for (int it = 0; it < 32; ++it) {
-        const int idx = it * 64 + lane, r = idx >> 4, ch = idx & 15;
-        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(reg + r * kEpiStride + ch * 16);
-        st_global<u32x4_t>(dst + ((size_t)r * ld) * sizeof(T) + ch * 16, x);
+      for (int it0 = 0; it0 < 32; it0 += 8) {
+        u32x4_t x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int idx = (it0 + k) * 64 + lane, r = idx >> 4, ch = idx & 15;
+          x[k] = *reinterpret_cast<const u32x4_t*>(reg + r * kEpiStride + ch * 16);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int idx = (it0 + k) * 64 + lane, r = idx >> 4, ch = idx & 15;
+          st_global<u32x4_t>(dst + ((size_t)r * ld) * sizeof(T) + ch * 16, x[k]);
+        }
       }
     };
     if constexpr (MODE == kApplyLast) {
