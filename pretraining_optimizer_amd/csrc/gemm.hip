@@ -198,11 +198,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
         b[j] = *reinterpret_cast<const u32x4_t*>(st + b_off + j * 32 * kRowBytes);
     }
   };
+  // bf16 B'X swaps the MFMA operands: block (i, j) then accumulates the
+  // transpose, so each lane holds 4 consecutive COLUMNS of one output row and
+  // the row-major epilogue writes 8 bytes per register group instead of 2.
+  constexpr bool kSwap = (MODE == kApply) && sizeof(T) == 2;
   auto mma = [&](const u32x4_t (&a)[4], const u32x4_t (&b)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Mfma<T>::run(acc[i][j], a[i], b[j]);
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (kSwap)
+          Mfma<T>::run(acc[i][j], b[j], a[i]);
+        else
+          Mfma<T>::run(acc[i][j], a[i], b[j]);
+      }
   };
   u32x4_t fa0[4], fb0[4], fa1[4], fb1[4];
 
@@ -366,7 +375,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   //   row = 32 i + 8 (r / 4) + 4 (lane / 32) + (r % 4),  col = 32 j + lane % 32
   // (inside the wavefront's 128 x 128 sub-tile): every group of 4 registers
   // is 4 consecutive rows of one column, i.e. 4 contiguous elements of the
-  // transposed layout.
+  // transposed layout.  With swapped operands (bf16 B'X) row and column trade
+  // places.
   float alpha = 1.0f;
   if (first_iter) {
     const float s = scal[pr.mat].s;
@@ -455,6 +465,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
               *reinterpret_cast<uint16_t*>(reg + (i * 32 + g * 8 + lg + e) * kEpiStride +
                                            (j * 32 + lc) * 2) = f32_to_bf16(acc[i][j][4 * g + e]);
     };
+    // Swapped accumulators (bf16 B'X): register group g of block (i, j) is
+    // row 32 i + lane % 32, columns 32 j + 8 g + 4 (lane / 32) + 0..3.
+    auto lds_rowmajor_swapped = [&]() {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            u32x2_t o;
+            o[0] = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+            o[1] = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+            *reinterpret_cast<u32x2_t*>(reg + (i * 32 + lc) * kEpiStride + (j * 32 + g * 8 + lg) * 2) = o;
+          }
+    };
     auto lds_transposed = [&]() {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -516,7 +541,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
         }
       }
     } else {
-      lds_rowmajor();
+      if constexpr (kSwap)
+        lds_rowmajor_swapped();
+      else
+        lds_rowmajor();
       store_rows(reinterpret_cast<uint8_t*>(pr.O) + ((size_t)wrow0 * pr.ldo + wcol0) * sizeof(T), pr.ldo);
       // The mirrored tile of the symmetric products (B' X keeps one layout).
       if (mirror) {
