@@ -269,10 +269,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     }
   };
   // Row i of this thread's share sits 4 KiB further in either Q layout.
-  auto sstore = [&](const u32x4_t (&r)[kLd], int slot, int operand) {
-    uint8_t* st = smem + slot * kStageBytes + operand * kOperandBytes + (operand ? sstq : sst);
+  // One base register per slot and operand layout, opaque to the compiler,
+  // so the operand and row offsets (< 64 KiB) go into the immediate offset
+  // field instead of a fresh address computation per write.
+  int wbase[2][2];
 #pragma unroll
-    for (int i = 0; i < kLd; ++i) *reinterpret_cast<u32x4_t*>(st + i * 4096) = r[i];
+  for (int sl = 0; sl < 2; ++sl) {
+    wbase[sl][0] = sl * kStageBytes + sst;
+    wbase[sl][1] = sl * kStageBytes + sstq;
+    asm volatile("" : "+v"(wbase[sl][0]), "+v"(wbase[sl][1]));
+  }
+  auto sstore = [&](const u32x4_t (&r)[kLd], int slot, int operand) {
+    MUONH_LDS uint8_t* base = lds + wbase[slot][operand];
+#pragma unroll
+    for (int i = 0; i < kLd; ++i)
+      *(MUONH_LDS u32x4_t*)(base + operand * kOperandBytes + i * 4096) = r[i];
   };
   // One K stage read from LDS slot `cur`; register set (ra, rb) holds the
   // next stage, which goes to slot `nxt`, and is then refilled with stage
@@ -282,6 +293,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   // K-major B fragments), the LDS writes and the global loads, a few at a
   // time, so no read waits long and the MFMA pipe stays fed.
   auto stage = [&](u32x4_t (&ra)[kLd], u32x4_t (&rb)[kLd], int cur, int nxt, int kt_load) {
+    __builtin_amdgcn_sched_barrier(0);
     // sub-step 0: + LDS writes of the P half of the next stage
     load_frag(fa1, fb1, cur, 1);
     mma(fa0, fb0);
