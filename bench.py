@@ -45,13 +45,14 @@ def per_kernel_work(shapes, ns_steps, tsize, gsize):
     Elementwise bytes per matrix (p = rows*cols, padded NS area q = m_pad*n_pad):
       momentum: read G (gsize p) + read/write M (8 p) + write X_0 (tsize q; the fp32
                 path also writes X_0^T, another tsize q)
-      reduce:   read W (4 p) + read u (tsize p)
       update:   read/write W (8 p) + read u (tsize p)
+    (<W,u>, ||u||^2 and ||W||^2 are reduced in the last B X launch's epilogue,
+    which reads W (4 p) beside its u stores: counted with that launch, not here.)
     """
     def pad(x):
         return (x + 255) // 256 * 256
     f = {"ns_gram": 0.0, "ns_poly": 0.0, "ns_apply": 0.0}
-    b = {"momentum": 0.0, "reduce": 0.0, "update": 0.0}
+    b = {"momentum": 0.0, "update": 0.0}
     params = 0
     for r, c in shapes:
         m, n = min(r, c), max(r, c)
@@ -62,7 +63,6 @@ def per_kernel_work(shapes, ns_steps, tsize, gsize):
         q = pad(m) * pad(n)
         params += p
         b["momentum"] += gsize * p + 8 * p + (1 if tsize == 2 else 2) * tsize * q
-        b["reduce"] += 4 * p + tsize * p
         b["update"] += 8 * p + tsize * p
     return f, b, params
 
@@ -267,11 +267,11 @@ def main():
         tf = fl[k] / launches[k] / (t_launch * 1e-3) / 1e12
         kern[k] = {"ms_per_launch": t_launch, "launches_per_step": launches[k],
                    "dense_tflops": tf, "frac_of_peak": tf / peak}
-    for k in ("momentum", "reduce", "update"):
+    for k in ("momentum", "update"):
         gbs = bytes_[k] / (per_step[k] * 1e-3) / 1e9
         kern[k] = {"ms": per_step[k], "gbs": gbs, "frac_of_hbm": gbs / PEAK_HBM_GBS}
     ns_ms = sum(per_step[k] for k in ("ns_gram", "ns_poly", "ns_apply", "ns_apply_last"))
-    el_ms = sum(per_step[k] for k in ("momentum", "reduce", "update"))
+    el_ms = sum(per_step[k] for k in ("momentum", "finalize", "update"))
     ns_tflops = info.ns_dense_flops / (ns_ms * 1e-3) / 1e12
     el_gbs = sum(bytes_.values()) / (el_ms * 1e-3) / 1e9
     alg_gbs = info.elem_bytes / (el_ms * 1e-3) / 1e9

@@ -164,7 +164,8 @@ int muonh_copy_update(muonh_handle* h, int32_t idx, void* dst_device, void* stre
  * steps since the last read into phases_ms[0..6] = momentum+pack (and its
  * finalise), NS X X^T, NS A A (each summed over the ns_steps launches), NS
  * B X (summed over the first ns_steps-1 launches), the last NS B X launch
- * (it writes u), reductions (+finalise), update; then clears the totals.
+ * (it writes u and reduces <W,u>, ||u||^2, ||W||^2 per tile), the finalise
+ * of those sums, update; then clears the totals.
  * n_phases must be >= 7.                                                    */
 int muonh_set_timing(muonh_handle* h, int32_t enable);
 int muonh_get_timing(muonh_handle* h, float* phases_ms, int32_t n_phases, int32_t* n_steps);

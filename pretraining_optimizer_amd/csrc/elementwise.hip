@@ -4,7 +4,8 @@
 //   momentum_kernel : M <- beta M + G, Y = M (or G + beta M), partial ||Y||^2,
 //                     Y packed as the first iterate X_0 in BOTH layouts the
 //                     grouped GEMM reads (X and X^T), zero-padded;
-//   reduce_kernel   : <W,u>, ||u||^2, ||W||^2 partials;
+//   (<W,u>, ||u||^2, ||W||^2 are reduced per tile by the last Newton-Schulz
+//   product's epilogue, gemm.hip);
 //   update_kernel   : W <- k1 W - k2 u  (Hyperball: k1 = R/||W~||,
 //                     k2 = k1 eta R / ||u||, from the closed form
 //                     ||W~||^2 = ||W||^2 - 2 k <W,u> + k^2 ||u||^2, k = eta R/||u||,
@@ -188,53 +189,17 @@ __global__ __launch_bounds__(64) void finalize_norm_kernel(const MatGeom* __rest
 // ---------------------------------------------------------------------------
 // flat chunk kernels over W (fp32, dense) and u (compact, ns dtype).
 
-template <typename T>
-__global__ __launch_bounds__(kElemThreads) void reduce_kernel(const Chunk* __restrict__ chunks,
-                                                              const MatGeom* __restrict__ geo,
-                                                              const MatPtrs* __restrict__ ptrs,
-                                                              double* __restrict__ partials) {
-  __shared__ double red[3][4];
-  const Chunk c = chunks[blockIdx.x];
-  const MatGeom& g = geo[c.mat];
-  const float* W = ptrs[c.mat].w + c.start;
-  const T* U = reinterpret_cast<const T*>(g.U) + c.start;
-  const int tid = threadIdx.x;
-  float wu = 0.0f, uu = 0.0f, ww = 0.0f;
-  const int n4 = c.len & ~3;
-  for (int i = tid * 4; i < n4; i += kElemThreads * 4) {
-    const f32x4_t w = Vec4<float>::load(W + i);
-    const f32x4_t u = Vec4<T>::load(U + i);
-    wu += w[0] * u[0] + w[1] * u[1] + w[2] * u[2] + w[3] * u[3];
-    uu += u[0] * u[0] + u[1] * u[1] + u[2] * u[2] + u[3] * u[3];
-    ww += w[0] * w[0] + w[1] * w[1] + w[2] * w[2] + w[3] * w[3];
-  }
-  for (int i = n4 + tid; i < c.len; i += kElemThreads) {
-    const float w = W[i];
-    float u;
-    if constexpr (sizeof(T) == 2) u = bf16_to_f32(U[i]); else u = U[i];
-    wu += w * u;
-    uu += u * u;
-    ww += w * w;
-  }
-  double v[3] = {(double)wu, (double)uu, (double)ww};
-  block_sum<3>(v, red);
-  if (tid == 0) {
-    partials[3 * (int64_t)blockIdx.x + 0] = v[0];
-    partials[3 * (int64_t)blockIdx.x + 1] = v[1];
-    partials[3 * (int64_t)blockIdx.x + 2] = v[2];
-  }
-}
-
 __global__ __launch_bounds__(64) void finalize_update_kernel(
     const MatGeom* __restrict__ geo, const double* __restrict__ partials,
     MatScalars* __restrict__ scal, muonh_stats* __restrict__ stats,
     const float* __restrict__ elr_scale, ElemParams prm) {
   const int mat = blockIdx.x;
   const MatGeom& g = geo[mat];
-  const double* p = partials + 3 * g.chunk0;
-  const double wu = ordered_sum(p + 0, g.nchunks, 3);
-  const double uu = ordered_sum(p + 1, g.nchunks, 3);
-  const double ww = ordered_sum(p + 2, g.nchunks, 3);
+  // per-(tile, wavefront) partials of the last B'X launch, in slot order
+  const double* p = partials + 3 * g.part0;
+  const double wu = ordered_sum(p + 0, g.nparts, 3);
+  const double uu = ordered_sum(p + 1, g.nparts, 3);
+  const double ww = ordered_sum(p + 2, g.nparts, 3);
   if (threadIdx.x != 0) return;
   const double R = scal[mat].R;
   const double eta = (double)prm.elr * (elr_scale ? (double)elr_scale[mat] : 1.0);
@@ -461,18 +426,6 @@ hipError_t launch_momentum(int bf16, const MomTile* tiles, int64_t ntiles, const
 hipError_t launch_finalize_norm(int32_t nmat, const MatGeom* geo, const double* partials,
                                 MatScalars* scal, float eps, hipStream_t st) {
   hipLaunchKernelGGL(finalize_norm_kernel, dim3(nmat), dim3(64), 0, st, geo, partials, scal, eps);
-  return hipGetLastError();
-}
-
-hipError_t launch_reduce(int bf16, const Chunk* chunks, int64_t nchunks, const MatGeom* geo,
-                         const MatPtrs* ptrs, double* partials, hipStream_t st) {
-  if (nchunks <= 0) return hipSuccess;
-  if (bf16)
-    hipLaunchKernelGGL(reduce_kernel<uint16_t>, dim3((unsigned)nchunks), dim3(kElemThreads), 0, st,
-                       chunks, geo, ptrs, partials);
-  else
-    hipLaunchKernelGGL(reduce_kernel<float>, dim3((unsigned)nchunks), dim3(kElemThreads), 0, st,
-                       chunks, geo, ptrs, partials);
   return hipGetLastError();
 }
 

@@ -103,6 +103,21 @@ constexpr int kBufferConfig = 0x00020000;
 constexpr int kSgMfma = 0x008, kSgVmemRead = 0x020, kSgDsRead = 0x100, kSgDsWrite = 0x200;
 #define MUONH_SG(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
+// Writes one wavefront's <W,u>, ||u||^2, ||W||^2 partial (fp64 xor-shuffle
+// tree over the lanes' fp32 sums, fixed order) to slot `slot`.
+__device__ __forceinline__ void write_stats(double* part, int64_t slot, float wu, float uu, float ww) {
+  double v[3] = {(double)wu, (double)uu, (double)ww};
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v[k] += __shfl_xor(v[k], off, 64);
+  if ((threadIdx.x & 63) == 0) {
+    part[3 * slot + 0] = v[0];
+    part[3 * slot + 1] = v[1];
+    part[3 * slot + 2] = v[2];
+  }
+}
+
 // One 16-byte LDS operand fragment x one 16-byte fragment -> 32x32 block.
 template <typename T> struct Mfma;
 template <> struct Mfma<uint16_t> {
@@ -129,7 +144,7 @@ template <typename T, int MODE>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     const GemmProb* __restrict__ probs, const GemmTile* __restrict__ tiles,
     const MatScalars* __restrict__ scal, int first_iter, int last_iter, int symmetric,
-    float ca, float cb, float cc) {
+    float ca, float cb, float cc, const MatPtrs* __restrict__ ptrs, double* __restrict__ part) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLdsBytes];
 
   const GemmTile t = tiles[blockIdx.x];
@@ -526,32 +541,87 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     if constexpr (MODE == kApplyLast) {
       // u, compact, in the matrix's own orientation: [um x un] (row-major
       // pass) or, for a tall matrix, [un x um] (transposed pass); rows and
-      // columns past the valid dims are dropped.
+      // columns past the valid dims are dropped.  The same pass reduces
+      // <W,u>, ||u||^2 and ||W||^2 over the stored (bf16) u and the matching
+      // W elements (U and W share the layout).  W is read in batches of 8
+      // rows of 8 per lane, double-buffered, the first batch issued before
+      // the sub-tile goes through LDS.
       int rbase, cbase, nrow, ncol, ld;
       if (!pr.u_tall) {
-        lds_rowmajor();
         rbase = wrow0; cbase = wcol0; nrow = pr.um; ncol = pr.un; ld = pr.un;
       } else {
-        lds_transposed();
         rbase = wcol0; cbase = wrow0; nrow = pr.un; ncol = pr.um; ld = pr.um;
       }
       uint16_t* U = reinterpret_cast<uint16_t*>(pr.U);
+      const float* W = ptrs[pr.mat].w;
       const bool vec_ok = (ld & 7) == 0;
-#pragma unroll 4
-      for (int it = 0; it < 32; ++it) {
-        const int idx = it * 64 + lane, r = idx >> 4, c0 = (idx & 15) * 8;
-        const int gr = rbase + r, gc = cbase + c0;
-        if (gr >= nrow || gc >= ncol) continue;
-        const u32x4_t x = *reinterpret_cast<const u32x4_t*>(reg + r * kEpiStride + c0 * 2);
-        uint16_t* d = U + (size_t)gr * ld + gc;
-        if (vec_ok && gc + 8 <= ncol) {
-          st_global<u32x4_t>(d, x);
-        } else {
+      // chunk `it` of the lane: sub-tile row it*4 + lane/16, columns 8 (lane%16) + 0..7
+      auto full = [&](int it) {
+        const int gr = rbase + it * 4 + (lane >> 4), gc = cbase + (lane & 15) * 8;
+        return vec_ok && gr < nrow && gc + 8 <= ncol;
+      };
+      auto wptr = [&](int it) {
+        return W + (size_t)(rbase + it * 4 + (lane >> 4)) * ld + cbase + (lane & 15) * 8;
+      };
+      f32x4_t wb[2][8][2];
+      auto wload = [&](int buf, int it0) {
 #pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (gc + q < ncol) st_global<uint16_t>(d + q, (uint16_t)(x[q >> 1] >> (16 * (q & 1))));
+        for (int k = 0; k < 8; ++k) {
+          if (full(it0 + k)) {
+            wb[buf][k][0] = ld_global<f32x4_t>(wptr(it0 + k));
+            wb[buf][k][1] = ld_global<f32x4_t>(wptr(it0 + k) + 4);
+          } else {
+            wb[buf][k][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            wb[buf][k][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+      };
+      wload(0, 0);
+      if (!pr.u_tall) lds_rowmajor(); else lds_transposed();
+      float swu = 0.0f, suu = 0.0f, sww = 0.0f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int cur = b & 1;
+        if (b + 1 < 4) wload(cur ^ 1, (b + 1) * 8);
+        u32x4_t x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int idx = (b * 8 + k) * 64 + lane;
+          x[k] = *reinterpret_cast<const u32x4_t*>(reg + (idx >> 4) * kEpiStride + (idx & 15) * 16);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int it = b * 8 + k;
+          const int gr = rbase + it * 4 + (lane >> 4), gc = cbase + (lane & 15) * 8;
+          if (gr >= nrow || gc >= ncol) continue;
+          uint16_t* d = U + (size_t)gr * ld + gc;
+          if (full(it)) {
+            st_global<u32x4_t>(d, x[k]);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              const float u = __uint_as_float((x[k][q >> 1] >> (16 * (q & 1))) << 16);
+              const float w = wb[cur][k][q >> 2][q & 3];
+              swu += w * u;
+              suu += u * u;
+              sww += w * w;
+            }
+          } else {
+            const float* wp = wptr(it);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (gc + q < ncol) {
+                const uint16_t h = (uint16_t)(x[k][q >> 1] >> (16 * (q & 1)));
+                st_global<uint16_t>(d + q, h);
+                const float u = __uint_as_float((uint32_t)h << 16), w = wp[q];
+                swu += w * u;
+                suu += u * u;
+                sww += w * w;
+              }
+          }
         }
       }
+      write_stats(part, (int64_t)pr.part0 + ((int64_t)t.tm * (pr.N / kGemmTile) + t.tn) * 4 + wave,
+                  swu, suu, sww);
     } else {
       if constexpr (kSwap)
         lds_rowmajor_swapped();
@@ -568,6 +638,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
     T* O = reinterpret_cast<T*>(MODE == kApplyLast ? pr.U : pr.O);
     T* OT = reinterpret_cast<T*>(pr.OT);
     const T* E = reinterpret_cast<const T*>(pr.E);
+    const float* W = (MODE == kApplyLast) ? ptrs[pr.mat].w : nullptr;
+    float swu = 0.0f, suu = 0.0f, sww = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -596,10 +668,15 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
             if (col < pr.un && row < pr.um) {
               const size_t base = pr.u_tall ? (size_t)col * pr.um + row : (size_t)row * pr.un + col;
               const size_t step = pr.u_tall ? 1 : (size_t)pr.un;
-              Vec4<T>::store1(O + base, v[0]);
-              if (row + 1 < pr.um) Vec4<T>::store1(O + base + step, v[1]);
-              if (row + 2 < pr.um) Vec4<T>::store1(O + base + 2 * step, v[2]);
-              if (row + 3 < pr.um) Vec4<T>::store1(O + base + 3 * step, v[3]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (row + e < pr.um) {
+                  Vec4<T>::store1(O + base + e * step, v[e]);   // + <W,u>, ||u||^2, ||W||^2 over it
+                  const float w = W[base + e * step];
+                  swu += w * v[e];
+                  suu += v[e] * v[e];
+                  sww += w * w;
+                }
             }
           } else {
 #pragma unroll
@@ -613,31 +690,35 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
         }
       }
     }
+    if constexpr (MODE == kApplyLast)
+      write_stats(part, (int64_t)pr.part0 + ((int64_t)t.tm * (pr.N / kGemmTile) + t.tn) * 4 + wave,
+                  swu, suu, sww);
   }
 }
 
 template <typename T>
 hipError_t launch_t(int mode, const GemmProb* probs, const GemmTile* tiles, int64_t ntiles,
                     const MatScalars* scal, int first_iter, int last_iter, int symmetric,
-                    float ca, float cb, float cc, hipStream_t st) {
+                    float ca, float cb, float cc, const MatPtrs* ptrs, double* part,
+                    hipStream_t st) {
   if (ntiles <= 0) return hipSuccess;
   const dim3 grid((unsigned)ntiles), block(kGemmThreads);
   switch (mode) {
     case kGram:
       hipLaunchKernelGGL((gemm_kernel<T, kGram>), grid, block, 0, st, probs, tiles, scal,
-                         first_iter, last_iter, symmetric, ca, cb, cc);
+                         first_iter, last_iter, symmetric, ca, cb, cc, ptrs, part);
       break;
     case kPoly:
       hipLaunchKernelGGL((gemm_kernel<T, kPoly>), grid, block, 0, st, probs, tiles, scal,
-                         first_iter, last_iter, symmetric, ca, cb, cc);
+                         first_iter, last_iter, symmetric, ca, cb, cc, ptrs, part);
       break;
     default:
       if (last_iter)
         hipLaunchKernelGGL((gemm_kernel<T, kApplyLast>), grid, block, 0, st, probs, tiles, scal,
-                           first_iter, last_iter, symmetric, ca, cb, cc);
+                           first_iter, last_iter, symmetric, ca, cb, cc, ptrs, part);
       else
         hipLaunchKernelGGL((gemm_kernel<T, kApply>), grid, block, 0, st, probs, tiles, scal,
-                           first_iter, last_iter, symmetric, ca, cb, cc);
+                           first_iter, last_iter, symmetric, ca, cb, cc, ptrs, part);
       break;
   }
   return hipGetLastError();
@@ -647,12 +728,13 @@ hipError_t launch_t(int mode, const GemmProb* probs, const GemmTile* tiles, int6
 
 hipError_t launch_gemm(int bf16, int mode, const GemmProb* probs, const GemmTile* tiles,
                        int64_t ntiles, const MatScalars* scal, int first_iter, int last_iter,
-                       int symmetric, float ca, float cb, float cc, hipStream_t st) {
+                       int symmetric, float ca, float cb, float cc, const MatPtrs* ptrs,
+                       double* part, hipStream_t st) {
   if (bf16)
     return launch_t<uint16_t>(mode, probs, tiles, ntiles, scal, first_iter, last_iter, symmetric,
-                              ca, cb, cc, st);
+                              ca, cb, cc, ptrs, part, st);
   return launch_t<float>(mode, probs, tiles, ntiles, scal, first_iter, last_iter, symmetric, ca,
-                         cb, cc, st);
+                         cb, cc, ptrs, part, st);
 }
 
 }  // namespace muonh

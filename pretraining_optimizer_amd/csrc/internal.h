@@ -43,6 +43,8 @@ struct GemmProb {
   int32_t um, un;  // valid (unpadded) NS dims m x n of the matrix (kPoly: um for the diagonal)
   int32_t u_tall;  // 1: U is [un x um] (the matrix is tall), 0: U is [um x un]
   int32_t mat;     // matrix index
+  int32_t part0;   // kApplyLast: first <W,u>/||u||^2/||W||^2 partial slot of the matrix
+                   // (one slot per output tile and wavefront)
 };
 
 // Tile list entry; prob < 0 marks an empty slot (XCD balancing padding).
@@ -78,6 +80,8 @@ struct MatGeom {
   int64_t mom_ntiles;
   int64_t chunk0;      // first flat chunk
   int64_t nchunks;
+  int64_t part0;       // first update-statistics partial slot (last B'X launch)
+  int64_t nparts;
 };
 
 // Per-step caller pointers (uploaded when they change).
@@ -109,9 +113,13 @@ struct ElemParams {
 // Kernel launchers (defined in the .hip files).  All return hipError_t of
 // the launch.
 
+// The last B'X launch also reduces <W,u>, ||u||^2 and ||W||^2 over each
+// tile's valid elements into `part` (3 doubles per tile and wavefront);
+// `ptrs` gives W.  Other launches ignore both.
 hipError_t launch_gemm(int bf16, int mode, const GemmProb* probs, const GemmTile* tiles,
                        int64_t ntiles, const MatScalars* scal, int first_iter, int last_iter,
-                       int symmetric, float ca, float cb, float cc, hipStream_t st);
+                       int symmetric, float ca, float cb, float cc, const MatPtrs* ptrs,
+                       double* part, hipStream_t st);
 
 hipError_t launch_momentum(int bf16, const MomTile* tiles, int64_t ntiles, const MatGeom* geo,
                            const MatPtrs* ptrs, double* partials, ElemParams prm, hipStream_t st);
@@ -119,8 +127,6 @@ hipError_t launch_momentum(int bf16, const MomTile* tiles, int64_t ntiles, const
 hipError_t launch_finalize_norm(int32_t nmat, const MatGeom* geo, const double* partials,
                                 MatScalars* scal, float eps, hipStream_t st);
 
-hipError_t launch_reduce(int bf16, const Chunk* chunks, int64_t nchunks, const MatGeom* geo,
-                         const MatPtrs* ptrs, double* partials, hipStream_t st);
 
 hipError_t launch_finalize_update(int32_t nmat, const MatGeom* geo, const double* partials,
                                   MatScalars* scal, muonh_stats* stats, const float* elr_scale,

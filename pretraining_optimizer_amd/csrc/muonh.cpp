@@ -60,6 +60,7 @@ struct MatPlan {
   float radius_in;
   size_t off_X[2], off_XT[2], off_A, off_B, off_U;
   int64_t mom_tile0, mom_ntiles, chunk0, nchunks;
+  int64_t part0, nparts;   // update-statistics partial slots (tile x wavefront of the last B'X)
 };
 
 struct Plan {
@@ -77,7 +78,8 @@ struct Plan {
   size_t off_geo, off_ptrs, off_scal, off_stats, off_need, off_elr;
   size_t off_mom_tiles, off_chunks, off_tiles[3];
   size_t off_probs_gram[2], off_probs_poly, off_probs_apply[2];
-  size_t off_part_mom, off_part_red;
+  size_t off_part_mom, off_part_red, off_part_upd;
+  int64_t nparts = 0;
   size_t total = 0;
 };
 
@@ -231,6 +233,12 @@ int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& op
     P.elem_bytes += (double)elems * ((m.g_bf16 ? 2.0 : 4.0) + 8.0 + 8.0);
   }
   P.n_buckets = (int)buckets.size();
+  // One partial slot per output tile and wavefront of the last B'X launch.
+  for (auto& m : P.mats) {
+    m.part0 = P.nparts;
+    m.nparts = (m.m_pad / kGemmTile) * (m.n_pad / kGemmTile) * (kGemmThreads / 64);
+    P.nparts += m.nparts;
+  }
 
   // GEMM tile lists.
   std::vector<std::tuple<int, int, int64_t>> d_gram, d_poly, d_apply;
@@ -273,6 +281,7 @@ int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& op
   for (int k = 0; k < 2; ++k) P.off_probs_apply[k] = take(sizeof(GemmProb) * n);
   P.off_part_mom = take(sizeof(double) * P.mom_tiles.size());
   P.off_part_red = take(sizeof(double) * 3 * P.chunks.size());
+  P.off_part_upd = take(sizeof(double) * 3 * (size_t)std::max<int64_t>(1, P.nparts));
   // Every Newton-Schulz buffer row is kRowSkewBytes longer than the padded
   // dim: with power-of-two pitches the 256 rows a tile streams at one K
   // offset would all land in the same L2 channel.
@@ -522,6 +531,8 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
     g.mom_ntiles = m.mom_ntiles;
     g.chunk0 = m.chunk0;
     g.nchunks = m.nchunks;
+    g.part0 = m.part0;
+    g.nparts = m.nparts;
     scal[i] = MatScalars{m.radius_in > 0.0f ? (double)m.radius_in : 0.0, 0.0, 1.0f, 1.0f, 0.0f, 0.0f};
     need[i] = m.radius_in > 0.0f ? 0 : 1;
     const int32_t M = (int32_t)m.m_pad, N = (int32_t)m.n_pad;
@@ -556,6 +567,7 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
       c.un = (int32_t)m.n;
       c.u_tall = m.tall;
       c.mat = i;
+      c.part0 = (int32_t)m.part0;
     }
     GemmProb& b = poly[i];
     std::memset(&b, 0, sizeof(b));
@@ -673,6 +685,7 @@ int muonh_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
   auto* geo = h->at<MatGeom>(pl.off_geo);
   auto* dptrs = h->at<MatPtrs>(pl.off_ptrs);
   auto* scal = h->at<MatScalars>(pl.off_scal);
+  auto* part_upd = h->at<double>(pl.off_part_upd);
   size_t evi = 0;
 #define LAUNCH(expr)                                                                        \
   do {                                                                                      \
@@ -690,21 +703,20 @@ int muonh_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
     const int first = it == 0, last = it == S - 1;
     LAUNCH(launch_gemm(bf, kGram, h->at<GemmProb>(pl.off_probs_gram[par]),
                        h->at<GemmTile>(pl.off_tiles[kGram]), (int64_t)pl.tiles[kGram].size(), scal,
-                       first, 0, pl.opt.symmetric, pl.opt.ns_a, pl.opt.ns_b, pl.opt.ns_c, st));
+                       first, 0, pl.opt.symmetric, pl.opt.ns_a, pl.opt.ns_b, pl.opt.ns_c, dptrs, part_upd, st));
     if ((rc = record(h, evi++, st))) return rc;
     LAUNCH(launch_gemm(bf, kPoly, h->at<GemmProb>(pl.off_probs_poly),
                        h->at<GemmTile>(pl.off_tiles[kPoly]), (int64_t)pl.tiles[kPoly].size(), scal,
-                       0, 0, pl.opt.symmetric, pl.opt.ns_a, pl.opt.ns_b, pl.opt.ns_c, st));
+                       0, 0, pl.opt.symmetric, pl.opt.ns_a, pl.opt.ns_b, pl.opt.ns_c, dptrs, part_upd, st));
     if ((rc = record(h, evi++, st))) return rc;
     LAUNCH(launch_gemm(bf, kApply, h->at<GemmProb>(pl.off_probs_apply[par]),
                        h->at<GemmTile>(pl.off_tiles[kApply]), (int64_t)pl.tiles[kApply].size(),
                        scal, first, last, pl.opt.symmetric, pl.opt.ns_a, pl.opt.ns_b, pl.opt.ns_c,
-                       st));
+                       dptrs, part_upd, st));
     if ((rc = record(h, evi++, st))) return rc;
   }
-  LAUNCH(launch_reduce(bf, h->at<Chunk>(pl.off_chunks), (int64_t)pl.chunks.size(), geo, dptrs,
-                       h->at<double>(pl.off_part_red), st));
-  LAUNCH(launch_finalize_update(n, geo, h->at<double>(pl.off_part_red), scal,
+  // <W,u>, ||u||^2 and ||W||^2 were reduced per tile by the last B'X launch.
+  LAUNCH(launch_finalize_update(n, geo, part_upd, scal,
                                 h->at<muonh_stats>(pl.off_stats), elr_scale_dev, prm, st));
   if ((rc = record(h, evi++, st))) return rc;
   LAUNCH(launch_update(bf, h->at<Chunk>(pl.off_chunks), (int64_t)pl.chunks.size(), geo, dptrs,

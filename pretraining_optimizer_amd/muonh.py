@@ -31,7 +31,7 @@ MUONH_MODE_HYPERBALL = 0
 MUONH_MODE_MUON_WD = 1
 MUONH_MODE_ELR_ALIGNED = 2
 
-PHASES = ("momentum", "ns_gram", "ns_poly", "ns_apply", "ns_apply_last", "reduce", "update")
+PHASES = ("momentum", "ns_gram", "ns_poly", "ns_apply", "ns_apply_last", "finalize", "update")
 
 
 class muonh_matrix_desc(ctypes.Structure):
