@@ -59,50 +59,59 @@ def test_ragged_shapes(ns, tol):
 
 
 @pytest.mark.parametrize("ns,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
-def test_stress_set_one_step(ns, tol):
-    """All 64 stress matrices in one grouped launch; the oracle checks a subset
-    (matrices are independent, so each checked one is an exact check)."""
-    announce(f"stress set, ns {ns}")
+def test_stress_set_trajectory(ns, tol):
+    """All 64 stress matrices in one grouped launch, 3 steps at eta 0.02; the
+    oracle follows a subset (matrices are independent, so each followed one
+    is an exact check): the 8 smallest, the 2 largest and the 2 most
+    elongated of each orientation."""
+    announce(f"stress set, ns {ns}, 3 steps")
     wl = inputs.workload("stress")
     mw, mg = workload_fns(wl)
     sizes = [r * c for r, c in wl.shapes]
     order = np.argsort(sizes)
-    check = sorted(set(order[:8].tolist() + order[-2:].tolist()))
-    reps = run_parity(wl.shapes, mw, mg, [0.02], check=check, ns=ns)
-    check_reports(reps, tol, [0.02])
+    aspect = np.array([r / c for r, c in wl.shapes])
+    ar = np.argsort(aspect)
+    check = sorted(set(order[:8].tolist() + order[-2:].tolist() + ar[:2].tolist() + ar[-2:].tolist()))
+    etas = [wl.eta(k) for k in range(wl.steps)]
+    reps = run_parity(wl.shapes, mw, mg, etas, check=check, ns=ns)
+    check_reports(reps, tol, etas)
 
 
 def test_diag170m_trajectory():
-    """170M-class set (84 matrices, bf16 grads scaled by 1/sqrt(fan_in)), 3 steps of the
-    linear ELR decay; the oracle follows layers 0 and 11."""
-    announce("diag170m, 3 steps")
+    """170M-class set (84 matrices, bf16 grads scaled by 1/sqrt(fan_in)), all 20
+    steps of the linear ELR decay; the oracle follows layers 0 and 11."""
+    announce("diag170m, 20 steps")
     wl = inputs.workload("diag170m")
     mw, mg = workload_fns(wl)
-    etas = [wl.eta(k) for k in range(3)]
+    etas = [wl.eta(k) for k in range(wl.steps)]
     check = list(range(7)) + list(range(77, 84))
     reps = run_parity(wl.shapes, mw, mg, etas, check=check, ns="bf16")
     check_reports(reps, TOL_BF16, etas)
 
 
-def test_qwen3_06b_two_steps():
-    announce("qwen3-0.6b set, 2 steps")
+def test_qwen3_06b_trajectory():
+    """Qwen3-0.6B set (196 matrices), all 10 steps of the linear decay from
+    0.024; the oracle follows the seven matrices of layer 0."""
+    announce("qwen3-0.6b set, 10 steps")
     wl = inputs.workload("qwen3_0.6b")
     mw, mg = workload_fns(wl)
-    etas = [wl.eta(k) for k in range(2)]
+    etas = [wl.eta(k) for k in range(wl.steps)]
     reps = run_parity(wl.shapes, mw, mg, etas, check=list(range(7)), ns="bf16")
     check_reports(reps, TOL_BF16, etas)
 
 
 def test_qwen3_17b_full_size():
     """The benchmarked configuration (196 Qwen3-1.7B matrices, bf16 NS) in the
-    same launch configuration the benchmark times; the oracle checks all seven
-    matrices of layer 0 (sampled outputs) and the norm invariant is checked on
-    all 196 matrices."""
-    announce("qwen3-1.7b full set, 2 steps")
+    same launch configuration the benchmark times, all 10 steps; the oracle
+    follows all seven matrices of layer 0 and q, k, v, o of layers 13 and 27
+    (each an exact check, matrices being independent), and the norm
+    invariant is checked on all 196 matrices after every step."""
+    announce("qwen3-1.7b full set, 10 steps")
     wl = inputs.workload("qwen3_1.7b")
     mw, mg = workload_fns(wl)
-    etas = [wl.eta(k) for k in range(2)]
-    reps = run_parity(wl.shapes, mw, mg, etas, check=list(range(7)), ns="bf16")
+    etas = [wl.eta(k) for k in range(wl.steps)]
+    check = list(range(7)) + [7 * l + j for l in (13, 27) for j in range(4)]
+    reps = run_parity(wl.shapes, mw, mg, etas, check=check, ns="bf16")
     check_reports(reps, TOL_BF16, etas)
     for rep in reps:
         assert len(rep.norm_err) == 196
