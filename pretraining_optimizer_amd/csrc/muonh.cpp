@@ -78,7 +78,7 @@ struct Plan {
   size_t off_geo, off_ptrs, off_scal, off_stats, off_need, off_elr;
   size_t off_mom_tiles, off_chunks, off_tiles[3];
   size_t off_probs_gram[2], off_probs_poly, off_probs_apply[2];
-  size_t off_part_mom, off_part_red, off_part_upd;
+  size_t off_part_mom, off_part_radius, off_part_upd;
   int64_t nparts = 0;
   size_t total = 0;
 };
@@ -280,7 +280,7 @@ int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& op
   P.off_probs_poly = take(sizeof(GemmProb) * n);
   for (int k = 0; k < 2; ++k) P.off_probs_apply[k] = take(sizeof(GemmProb) * n);
   P.off_part_mom = take(sizeof(double) * P.mom_tiles.size());
-  P.off_part_red = take(sizeof(double) * 3 * P.chunks.size());
+  P.off_part_radius = take(sizeof(double) * P.chunks.size());   // one ||W_0||^2 partial per chunk
   P.off_part_upd = take(sizeof(double) * 3 * (size_t)std::max<int64_t>(1, P.nparts));
   // Every Newton-Schulz buffer row is kRowSkewBytes longer than the padded
   // dim: with power-of-two pitches the 256 rows a tile streams at one K
@@ -613,9 +613,9 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
     h->cur_ptrs = ptrs;
     h->ptrs_valid = true;
     hipError_t e = launch_radius(h->at<Chunk>(pl.off_chunks), (int64_t)pl.chunks.size(),
-                                 h->at<MatPtrs>(pl.off_ptrs), h->at<double>(pl.off_part_red), st);
+                                 h->at<MatPtrs>(pl.off_ptrs), h->at<double>(pl.off_part_radius), st);
     if (e == hipSuccess)
-      e = launch_finalize_radius(n, h->at<MatGeom>(pl.off_geo), h->at<double>(pl.off_part_red),
+      e = launch_finalize_radius(n, h->at<MatGeom>(pl.off_geo), h->at<double>(pl.off_part_radius),
                                  h->at<int32_t>(pl.off_need), h->at<MatScalars>(pl.off_scal), st);
     if (e != hipSuccess)
       return bail(fail(MUONH_EHIP, std::string("radius kernels: ") + hipGetErrorString(e)));
