@@ -242,10 +242,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   constexpr int kLd = kOperandBytes / 16 / kGemmThreads;   // 8 loads per operand
   const int srow = tid >> 3, schunk = tid & 7;
   const int qrow = tid >> 5, qchunk = tid & 31;
-  // Operand loads are buffer loads: a uniform base (the tile's panel) in the
-  // descriptor, a per-thread byte offset fixed for the whole tile and a
-  // uniform per-load offset, so no vector address arithmetic is issued
-  // between the MFMAs.  Offsets stay below 2^31 (a panel spans < 32 MiB).
+  // Operand loads are buffer loads: a uniform base in the descriptor, a
+  // per-thread byte offset fixed for the whole tile and a uniform per-load
+  // offset, so no vector address arithmetic is issued between the MFMAs.
+  // Offsets stay below 2^31: a row-major operand's base is the tile's panel
+  // (256 rows of at most 64 Ki + 32 elements: < 70 MB), and the K-major
+  // X of bf16 B'X gets a new base at every stage (64 rows), since the whole
+  // of X can exceed 2 GiB.
   const uint8_t* pbase = reinterpret_cast<const uint8_t*>(pr.P) + (size_t)row0 * pstride;
   const uint8_t* qbase = kQT ? reinterpret_cast<const uint8_t*>(pr.Q) + (size_t)col0 * sizeof(T)
                              : reinterpret_cast<const uint8_t*>(pr.Q) + (size_t)col0 * qstride;
@@ -275,8 +278,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   auto gload_q = [&](u32x4_t (&r)[kLd], int kt) {
     if constexpr (kQT) {
       const size_t k0 = (size_t)min(kt, nk - 1) * kTrRows;
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(qbase + k0 * qstride), (short)0, -1, kBufferConfig);
 #pragma unroll
-      for (int i = 0; i < kLd; ++i) r[i] = bload(qrs, qvoff, (k0 + i * 8) * qstride);
+      for (int i = 0; i < kLd; ++i) r[i] = bload(rs, qvoff, (size_t)(i * 8) * qstride);
     } else {
       const size_t koff = (size_t)min(kt, nk - 1) * kRowBytes;
 #pragma unroll

@@ -15,7 +15,7 @@ import torch
 import inputs
 import oracle
 import pretraining_optimizer_amd as pm
-from parity import (TOL_BF16, TOL_F32, announce, check_reports, rel, run_parity, unit,
+from parity import (TOL_BF16, TOL_F32, TOL_NORM, announce, check_reports, rel, run_parity, unit,
                     workload_fns)
 
 pytestmark = pytest.mark.gpu
@@ -250,4 +250,50 @@ def test_step_list_mismatch_is_rejected():
     assert lib.muonh_step(opt._h, d, 2, ctypes.byref(args), None) == mb.MUONH_EMISMATCH
     d[0].g = ws[0].data_ptr() + 4   # misaligned
     assert lib.muonh_step(opt._h, d, 1, ctypes.byref(args), None) == mb.MUONH_EINVAL
+    opt.close()
+
+
+def test_iterate_beyond_2gib_signed_permutation():
+    """A 32768 x 33024 matrix, so the bf16 iterate X (2.17 GB) spans more than
+    2^31 bytes and the operand walking X along K must rebase its addresses.
+    G is a signed permutation of the first 32768 columns (the rest zero): its
+    rows are orthogonal with equal norms, so X X^T, A A and B' are multiples
+    of I at every iteration, every product keeps X proportional to G and each
+    bf16 rounding is a uniform scaling.  Hence u^ = G/||G|| to fp32 rounding
+    at any size (the polynomial acts on one repeated singular value), the
+    zero columns stay exactly zero, and W follows the Hyperball closed form
+    with ||W|| = R."""
+    announce("iterate > 2 GiB: 32768 x 33024 signed permutation")
+    dev = torch.device("cuda")
+    r, c = 32768, 33024
+    gen = torch.Generator(device=dev).manual_seed(7)
+    perm = torch.randperm(r, generator=gen, device=dev)
+    sign = torch.randint(0, 2, (r,), generator=gen, device=dev).to(torch.bfloat16) * 2 - 1
+    g = torch.zeros((r, c), device=dev, dtype=torch.bfloat16)
+    g[torch.arange(r, device=dev), perm] = sign
+    w = torch.randn((r, c), generator=gen, device=dev)
+    m = torch.zeros_like(w)
+    R = float(torch.linalg.vector_norm(w, dtype=torch.float64))
+    eta = 0.02
+    opt = pm.MuonH([w], [m], grad_dtype=torch.bfloat16)
+    assert abs(opt.radii()[0] / R - 1.0) < 1e-6
+    w_tilde = w.double()                       # W_0 in fp64; the step updates w in place
+    opt.step([g], eta)
+    u = opt.copy_update(0)
+    torch.cuda.synchronize()
+    assert torch.equal(m, g.float())           # M = beta * 0 + G
+    assert bool((u[:, r:] == 0).all())
+    uhat = u / torch.linalg.vector_norm(u, dtype=torch.float64).item()
+    ghat = g.float() / float(r) ** 0.5
+    err = torch.linalg.vector_norm((uhat - ghat).double()).item()
+    announce(f"u^ error {err:.3e}")
+    assert err <= 1e-5, err
+    del uhat, u
+    w_tilde.sub_(ghat.double(), alpha=eta * R)
+    w_exp = w_tilde.mul_(R / torch.linalg.vector_norm(w_tilde).item())
+    werr = (torch.linalg.vector_norm(w.double() - w_exp) / R).item()
+    wn = torch.linalg.vector_norm(w, dtype=torch.float64).item()
+    announce(f"W error {werr:.3e}, |W|/R - 1 {wn / R - 1:.2e}")
+    assert werr <= 1e-5 and abs(wn / R - 1.0) <= TOL_NORM
+    assert opt.stats()[0]["nonfinite"] == 0
     opt.close()
