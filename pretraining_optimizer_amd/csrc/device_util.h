@@ -44,17 +44,25 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float((uint32_t)h << 16);
 }
 
-// 4 consecutive elements of type T <-> 4 floats.
+// 4 consecutive elements of type T <-> 4 floats.  The *_nt forms are
+// non-temporal (streaming) accesses for data a kernel touches once (the
+// elementwise kernels' W, M, G and u streams), so they do not displace
+// cached data; the Newton-Schulz operands use the ordinary forms.
 template <typename T> struct Vec4;
 template <> struct Vec4<uint16_t> {
-  static __device__ __forceinline__ f32x4_t load(const uint16_t* p) {
-    const u32x2_t v = ld_global<u32x2_t>(p);
+  static __device__ __forceinline__ f32x4_t widen(u32x2_t v) {
     f32x4_t r;
     r[0] = __uint_as_float(v[0] << 16);
     r[1] = __uint_as_float(v[0] & 0xffff0000u);
     r[2] = __uint_as_float(v[1] << 16);
     r[3] = __uint_as_float(v[1] & 0xffff0000u);
     return r;
+  }
+  static __device__ __forceinline__ f32x4_t load(const uint16_t* p) {
+    return widen(ld_global<u32x2_t>(p));
+  }
+  static __device__ __forceinline__ f32x4_t load_nt(const uint16_t* p) {
+    return widen(__builtin_nontemporal_load((const MUONH_GLOBAL u32x2_t*)p));
   }
   static __device__ __forceinline__ void store(uint16_t* p, f32x4_t v) {
     u32x2_t o;
@@ -72,6 +80,12 @@ template <> struct Vec4<float> {
   }
   static __device__ __forceinline__ void store(float* p, f32x4_t v) {
     st_global<f32x4_t>(p, v);
+  }
+  static __device__ __forceinline__ f32x4_t load_nt(const float* p) {
+    return __builtin_nontemporal_load((const MUONH_GLOBAL f32x4_t*)p);
+  }
+  static __device__ __forceinline__ void store_nt(float* p, f32x4_t v) {
+    __builtin_nontemporal_store(v, (MUONH_GLOBAL f32x4_t*)p);
   }
   static __device__ __forceinline__ void store1(float* p, float v) { st_global<float>(p, v); }
 };

@@ -53,7 +53,7 @@ __device__ __forceinline__ void block_sum(double (&v)[NV], double (*red)[4]) {
 template <typename G> struct GradLoad;
 template <> struct GradLoad<uint16_t> {
   static __device__ __forceinline__ f32x4_t load4(const void* p, int64_t off) {
-    return Vec4<uint16_t>::load(reinterpret_cast<const uint16_t*>(p) + off);
+    return Vec4<uint16_t>::load_nt(reinterpret_cast<const uint16_t*>(p) + off);
   }
   static __device__ __forceinline__ float load1(const void* p, int64_t off) {
     return bf16_to_f32(reinterpret_cast<const uint16_t*>(p)[off]);
@@ -61,7 +61,7 @@ template <> struct GradLoad<uint16_t> {
 };
 template <> struct GradLoad<float> {
   static __device__ __forceinline__ f32x4_t load4(const void* p, int64_t off) {
-    return Vec4<float>::load(reinterpret_cast<const float*>(p) + off);
+    return Vec4<float>::load_nt(reinterpret_cast<const float*>(p) + off);
   }
   static __device__ __forceinline__ float load1(const void* p, int64_t off) {
     return reinterpret_cast<const float*>(p)[off];
@@ -101,7 +101,7 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, const MatGeom& g
     if (full[q]) {
       const int64_t off = row * g.cols + col;
       gv[q] = GradLoad<G>::load4(p.g, off);
-      mv[q] = Vec4<float>::load(p.m + off);
+      mv[q] = Vec4<float>::load_nt(p.m + off);
     }
   }
 #pragma unroll
@@ -112,7 +112,7 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, const MatGeom& g
     const int64_t off = row * g.cols + col;
     if (full[q]) {
       const f32x4_t m = beta * mv[q] + gv[q];
-      Vec4<float>::store(p.m + off, m);
+      Vec4<float>::store_nt(p.m + off, m);
       y = prm.nesterov ? gv[q] + beta * m : m;
     } else if (row < g.rows) {
 #pragma unroll
@@ -267,16 +267,16 @@ __global__ __launch_bounds__(kElemThreads) void update_kernel(const Chunk* __res
     f32x4_t w[4], u[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      w[k] = Vec4<float>::load(W + i + k * kStep);
-      u[k] = Vec4<T>::load(U + i + k * kStep);
+      w[k] = Vec4<float>::load_nt(W + i + k * kStep);
+      u[k] = Vec4<T>::load_nt(U + i + k * kStep);
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) Vec4<float>::store(W + i + k * kStep, k1 * w[k] - k2 * u[k]);
+    for (int k = 0; k < 4; ++k) Vec4<float>::store_nt(W + i + k * kStep, k1 * w[k] - k2 * u[k]);
   }
   for (; i < n4; i += kStep) {
-    const f32x4_t w = Vec4<float>::load(W + i);
-    const f32x4_t u = Vec4<T>::load(U + i);
-    Vec4<float>::store(W + i, k1 * w - k2 * u);
+    const f32x4_t w = Vec4<float>::load_nt(W + i);
+    const f32x4_t u = Vec4<T>::load_nt(U + i);
+    Vec4<float>::store_nt(W + i, k1 * w - k2 * u);
   }
   for (int j = n4 + tid; j < c.len; j += kElemThreads) {
     float u;
@@ -363,27 +363,27 @@ __device__ __forceinline__ void adamw_chunk(const Chunk& c, const AdamwPtrs& q,
     f32x4_t w[2], m[2], v[2], g[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      w[k] = Vec4<float>::load(W + i + k * kStep);
-      m[k] = Vec4<float>::load(Mm + i + k * kStep);
-      v[k] = Vec4<float>::load(V + i + k * kStep);
-      g[k] = Vec4<G>::load(Gp + i + k * kStep);
+      w[k] = Vec4<float>::load_nt(W + i + k * kStep);
+      m[k] = Vec4<float>::load_nt(Mm + i + k * kStep);
+      v[k] = Vec4<float>::load_nt(V + i + k * kStep);
+      g[k] = Vec4<G>::load_nt(Gp + i + k * kStep);
     }
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       adamw4(w[k], m[k], v[k], g[k], p);
-      Vec4<float>::store(W + i + k * kStep, w[k]);
-      Vec4<float>::store(Mm + i + k * kStep, m[k]);
-      Vec4<float>::store(V + i + k * kStep, v[k]);
+      Vec4<float>::store_nt(W + i + k * kStep, w[k]);
+      Vec4<float>::store_nt(Mm + i + k * kStep, m[k]);
+      Vec4<float>::store_nt(V + i + k * kStep, v[k]);
     }
   }
   for (; i < n4; i += kStep) {
-    f32x4_t w = Vec4<float>::load(W + i), m = Vec4<float>::load(Mm + i);
-    f32x4_t v = Vec4<float>::load(V + i);
-    const f32x4_t g = Vec4<G>::load(Gp + i);
+    f32x4_t w = Vec4<float>::load_nt(W + i), m = Vec4<float>::load_nt(Mm + i);
+    f32x4_t v = Vec4<float>::load_nt(V + i);
+    const f32x4_t g = Vec4<G>::load_nt(Gp + i);
     adamw4(w, m, v, g, p);
-    Vec4<float>::store(W + i, w);
-    Vec4<float>::store(Mm + i, m);
-    Vec4<float>::store(V + i, v);
+    Vec4<float>::store_nt(W + i, w);
+    Vec4<float>::store_nt(Mm + i, m);
+    Vec4<float>::store_nt(V + i, v);
   }
   for (int j = n4 + tid; j < c.len; j += kElemThreads) {
     float g;
