@@ -29,6 +29,11 @@
  *   - Work is enqueued asynchronously; errors from kernels surface at the
  *     next synchronising call (muonh_get_radii / muonh_get_stats).
  *   - A handle is not thread-safe; distinct handles are independent.
+ *   - Environment, read at init: MUONH_DEBUG_SYNC=1 synchronises the stream
+ *     after every kernel launch so a device fault is reported (MUONH_EHIP) by
+ *     the step that caused it, naming the launch (slow; for debugging);
+ *     MUONH_LOG=1 prints the plan (buckets, tile and chunk counts, workspace,
+ *     FLOP per step) on stderr.
  */
 #ifndef MUONH_H_
 #define MUONH_H_

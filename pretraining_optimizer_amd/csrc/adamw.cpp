@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -32,6 +33,7 @@ struct muonh_adamw_handle {
   bool ptrs_valid = false;
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
+  bool debug_sync = false;            // MUONH_DEBUG_SYNC=1: synchronise after the launch
 };
 
 namespace {
@@ -102,6 +104,7 @@ int muonh_adamw_init(muonh_adamw_handle** out, const muonh_adamw_tensor* t, int3
   auto* h = new muonh_adamw_handle();
   h->n = n;
   h->opt = o;
+  if (const char* e = std::getenv("MUONH_DEBUG_SYNC")) h->debug_sync = std::atoi(e) != 0;
   for (int32_t i = 0; i < n; ++i) {
     h->numel.push_back(t[i].numel);
     h->g_bf16.push_back(t[i].g_dtype == MUONH_BF16 ? 1 : 0);
@@ -177,6 +180,7 @@ int muonh_adamw_step(muonh_adamw_handle* h, const muonh_adamw_tensor* t, int32_t
   prm.step_size = (float)((double)lr / bc1);
   prm.rbc2 = (float)(1.0 / std::sqrt(bc2));
   ADAMW_HIP(launch_adamw(h->d_chunks, (int64_t)h->chunks.size(), h->d_ptrs, prm, st));
+  if (h->debug_sync) ADAMW_HIP(hipStreamSynchronize(st));
   return MUONH_OK;
 }
 

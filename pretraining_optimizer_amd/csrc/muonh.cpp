@@ -13,6 +13,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <string>
@@ -331,6 +332,9 @@ struct muonh_handle {
   int ev_cur = 0;
   double phase_total[7] = {0, 0, 0, 0, 0, 0, 0};
   int32_t timed_steps = 0;
+  // MUONH_DEBUG_SYNC=1: synchronise after every launch and report which
+  // kernel failed (slow; for attributing device faults).
+  bool debug_sync = false;
 
   template <typename T> T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
 };
@@ -478,6 +482,19 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
   h->plan = std::move(P);
   h->device = dev;
   const Plan& pl = h->plan;
+  if (const char* e = std::getenv("MUONH_DEBUG_SYNC")) h->debug_sync = std::atoi(e) != 0;
+  if (const char* e = std::getenv("MUONH_LOG"); e && std::atoi(e) != 0) {
+    // MUONH_LOG=1: the plan on stderr.
+    size_t gt[3] = {0, 0, 0};
+    for (int k = 0; k < 3; ++k)
+      for (const auto& t : pl.tiles[k]) gt[k] += t.prob >= 0;
+    std::fprintf(stderr,
+                 "muonh: %d matrices in %d shape buckets, ns %s x%d; GEMM tiles gram %zu poly %zu "
+                 "apply %zu; %zu momentum tiles, %zu chunks; workspace %.3f GB; NS %.3e dense / "
+                 "%.3e executed FLOP per step\n",
+                 n, pl.n_buckets, pl.bf16 ? "bf16" : "fp32", pl.opt.ns_steps, gt[0], gt[1], gt[2],
+                 pl.mom_tiles.size(), pl.chunks.size(), pl.total / 1e9, pl.ns_dense, pl.ns_exec);
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   auto bail = [&](int code) {
     muonh_destroy(h);
@@ -690,6 +707,7 @@ int muonh_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
 #define LAUNCH(expr)                                                                        \
   do {                                                                                      \
     hipError_t e_ = (expr);                                                                 \
+    if (e_ == hipSuccess && h->debug_sync) e_ = hipStreamSynchronize(st);                   \
     if (e_ != hipSuccess) return fail(MUONH_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
   } while (0)
 

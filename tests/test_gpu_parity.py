@@ -297,3 +297,30 @@ def test_iterate_beyond_2gib_signed_permutation():
     assert werr <= 1e-5 and abs(wn / R - 1.0) <= TOL_NORM
     assert opt.stats()[0]["nonfinite"] == 0
     opt.close()
+
+
+def test_debug_sync_and_log_flags(monkeypatch, capfd):
+    """MUONH_DEBUG_SYNC=1 (a synchronisation after every launch) gives
+    bitwise the same steps as the asynchronous path, and MUONH_LOG=1 prints
+    the plan at init."""
+    announce("MUONH_DEBUG_SYNC / MUONH_LOG")
+    shapes = [(300, 200), (128, 640)]
+    mw, mg = _gauss_fns(shapes, torch.bfloat16, seed=6)
+    outs = []
+    for flags in ({}, {"MUONH_DEBUG_SYNC": "1", "MUONH_LOG": "1"}):
+        for name in ("MUONH_DEBUG_SYNC", "MUONH_LOG"):
+            monkeypatch.delenv(name, raising=False)
+        for name, value in flags.items():
+            monkeypatch.setenv(name, value)
+        ws = [mw(i).cuda() for i in range(len(shapes))]
+        ms = [torch.zeros_like(w) for w in ws]
+        opt = pm.MuonH(ws, ms, grad_dtype=torch.bfloat16)
+        for k in range(2):
+            opt.step([mg(k, i).cuda() for i in range(len(shapes))], 0.02)
+        torch.cuda.synchronize()
+        opt.close()
+        outs.append([w.clone() for w in ws] + [m.clone() for m in ms])
+    err = capfd.readouterr().err
+    assert "muonh: 2 matrices" in err, err
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)

@@ -272,3 +272,46 @@ def test_wsd_and_cosine_shapes():
     assert oracle.lr_cosine(0, 100, 1e-5, 1e-7) == pytest.approx(1e-5)
     assert oracle.lr_cosine(50, 100, 1e-5, 1e-7) == pytest.approx(0.5 * (1e-5 + 1e-7))
     assert oracle.lr_cosine(100, 100, 1e-5, 1e-7) == pytest.approx(1e-7)
+
+
+# ---------------------------------------------------------------------------
+# Property tests over random small shapes, spectra and step sizes.
+
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+_SETTINGS = settings(max_examples=40, deadline=None, derandomize=True)
+
+
+@_SETTINGS
+@given(r=st.integers(1, 24), c=st.integers(1, 24), seed=st.integers(0, 2 ** 31 - 1),
+       decades=st.floats(0.0, 3.0), steps=st.integers(1, 6))
+def test_ns_closed_form_random_shapes_and_spectra(r, c, seed, decades, steps):
+    """Any shape (1 x n, n x 1, square, tall, wide), singular values spread
+    over up to three decades, any iteration count: the oracle's Newton-Schulz
+    equals the SVD closed form U p^steps(sigma/(||Y||+eps)) V^T."""
+    rng = np.random.default_rng(seed)
+    k = min(r, c)
+    s = 10.0 ** (-decades * rng.random(k))
+    y = _with_singular_values(rng, r, c, s) if k > 1 else rng.standard_normal((r, c))
+    got = oracle.newton_schulz(y, steps)
+    assert _rel(got, _svd_closed_form(y, steps)) <= 1e-10
+
+
+@_SETTINGS
+@given(r=st.integers(1, 20), c=st.integers(1, 20), seed=st.integers(0, 2 ** 31 - 1),
+       eta=st.floats(1e-4, 0.5))
+def test_hyperball_invariants_random(r, c, seed, eta):
+    """For any W, direction and step size: ||W_{t+1}|| = R, the pre-projection
+    displacement is eta R (ELR = eta), and the new W is the projection of
+    W - eta R u^ onto the sphere (positive multiple, unit cosine)."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((r, c))
+    R = float(np.linalg.norm(w)) * (0.5 + rng.random())
+    w = w * (R / np.linalg.norm(w))
+    u = rng.standard_normal((r, c))
+    w1, _ = om.hyperball_update(w, u, eta, R)
+    assert abs(np.linalg.norm(w1) / R - 1.0) <= 1e-12
+    wt = w - eta * R * u / np.linalg.norm(u)
+    assert abs(np.linalg.norm(wt - w) / R - eta) <= 1e-12
+    cos = float(np.sum(w1 * wt)) / (np.linalg.norm(w1) * np.linalg.norm(wt))
+    assert abs(cos - 1.0) <= 1e-12
