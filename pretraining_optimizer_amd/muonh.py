@@ -84,7 +84,7 @@ class muonh_plan_info(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
-_lib = None
+_libs = {}
 
 # (name, restype, argtypes)
 _SIGNATURES = [
@@ -122,10 +122,10 @@ _SIGNATURES = [
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libmuonh.so; raises if it has not been built."""
-    global _lib
-    if _lib is not None:
-        return _lib
+    """Load libmuonh.so (once per path); raises if it has not been built."""
+    path = os.path.abspath(path)
+    if path in _libs:
+        return _libs[path]
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m pretraining_optimizer_amd.build`"
                            " (or __graft_entry__.build()); there is no fallback path")
@@ -134,7 +134,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
+    _libs[path] = lib
     return lib
 
 
@@ -206,6 +206,17 @@ def _stream_ptr(stream) -> int:
     return int(s.cuda_stream)
 
 
+def _record(stream, tensors):
+    """Work enqueued on a stream other than torch's current one reads and
+    writes these tensors asynchronously: tell torch's caching allocator, so
+    their memory is not handed out again before that stream has passed them."""
+    import torch
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        t.record_stream(stream)
+
+
 class MuonH:
     """One MuonH optimizer over a list of fp32 CUDA matrices (W, M in place).
 
@@ -259,6 +270,7 @@ class MuonH:
             d[i].w = self.weights[i].data_ptr()
             d[i].g = g.data_ptr()
             d[i].m = self.moms[i].data_ptr()
+        _record(stream, list(grads) + self.weights + self.moms)
         args = muonh_step_args()
         args.elr = float(elr)
         scale_arr = None
@@ -284,6 +296,7 @@ class MuonH:
         import torch
         r, c = self.shapes[idx]
         dst = torch.empty((r, c), dtype=torch.float32, device=self.weights[idx].device)
+        _record(stream, [dst])
         _check(self._lib.muonh_copy_update(self._h, idx, dst.data_ptr(), _stream_ptr(stream)),
                "muonh_copy_update")
         return dst
@@ -372,6 +385,7 @@ class AdamW:
             d[i].g = g.data_ptr()
             d[i].m = self.exp_avgs[i].data_ptr()
             d[i].v = self.exp_avg_sqs[i].data_ptr()
+        _record(stream, list(grads) + self.params + self.exp_avgs + self.exp_avg_sqs)
         _check(self._lib.muonh_adamw_step(self._h, d, self.n, float(lr), int(step), _stream_ptr(stream)),
                "muonh_adamw_step")
 

@@ -324,3 +324,33 @@ def test_debug_sync_and_log_flags(monkeypatch, capfd):
     assert "muonh: 2 matrices" in err, err
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def test_steps_on_a_side_stream():
+    """Steps enqueued on a stream other than torch's current one, with each
+    step's gradients dropped right after the call (the binding records them
+    on that stream), give bitwise the results of the current-stream path."""
+    announce("side stream")
+    shapes = [(256, 384), (640, 256)]
+    mw, mg = _gauss_fns(shapes, torch.bfloat16, seed=8)
+    outs = []
+    for side in (False, True):
+        ws = [mw(i).cuda() for i in range(len(shapes))]
+        ms = [torch.zeros_like(w) for w in ws]
+        s = torch.cuda.Stream() if side else None
+        if side:
+            s.wait_stream(torch.cuda.current_stream())
+        opt = pm.MuonH(ws, ms, grad_dtype=torch.bfloat16, stream=s)
+        for k in range(3):
+            gs = [mg(k, i).cuda() for i in range(len(shapes))]
+            if side:
+                s.wait_stream(torch.cuda.current_stream())
+            opt.step(gs, 0.02, stream=s)
+            del gs
+        if side:
+            torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        opt.close()
+        outs.append([w.clone() for w in ws] + [m.clone() for m in ms])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
