@@ -117,6 +117,20 @@ def test_qwen3_17b_full_size():
         assert len(rep.norm_err) == 196
 
 
+def test_qwen3_17b_fp32_newton_schulz():
+    """The benchmarked 1.7B set with the fp32 Newton-Schulz path (fp32 MFMA,
+    X and X^T both stored), 2 steps; the oracle follows layer 0 to the fp32
+    tolerance and the norm invariant is checked on all 196 matrices."""
+    announce("qwen3-1.7b full set, fp32 Newton-Schulz, 2 steps")
+    wl = inputs.workload("qwen3_1.7b")
+    mw, mg = workload_fns(wl)
+    etas = [wl.eta(k) for k in range(2)]
+    reps = run_parity(wl.shapes, mw, mg, etas, check=list(range(7)), ns="f32")
+    check_reports(reps, TOL_F32, etas)
+    for rep in reps:
+        assert len(rep.norm_err) == 196
+
+
 def test_qwen3_17b_fused_projections():
     """Qwen3-1.7B dims with fused qkv (4096 x 2048) and gate_up (12288 x 2048)
     matrices: wider Newton-Schulz problems (n up to 12288) in the same grouped
