@@ -15,9 +15,10 @@ Sources (the pages are cited by title and section / equation only):
 
 Every function here is pinned by a ``-m "not gpu"`` test against something
 other than itself (SVD closed forms, textbook special cases, invariants,
-values printed on the pages).  The one choice no page fixes -- the
-Newton-Schulz coefficients -- is "parity unpinned" against the authors' runs;
-only its mathematics is pinned.
+values printed on the pages).  The one choice no page fixes is the
+Newton-Schulz coefficient values (a reading, configurable): the functions
+that use them are pinned by their mathematics for any coefficients, but which
+values the authors ran cannot be checked from the pages.
 """
 
 from .muonh import (  # noqa: F401

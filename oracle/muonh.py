@@ -41,7 +41,8 @@ from typing import Iterable, Optional, Sequence
 import numpy as np
 
 # Quintic coefficients of the published Muon method (Jordan et al., 2024).
-# The pages do not print them: parity unpinned against the authors' runs.
+# The pages do not print them (a reading); newton_schulz itself is pinned for
+# any coefficients by the SVD closed form and the classical polar limit.
 NS_COEFFS_QUINTIC = (3.4445, -4.7750, 2.0315)
 # Classical Newton-Schulz polar iteration written in the same quintic form:
 # p(x) = (15 x - 10 x^3 + 3 x^5) / 8, with p(1) = 1 and p'(1) = 0, whose
