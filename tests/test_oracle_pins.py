@@ -315,3 +315,75 @@ def test_hyperball_invariants_random(r, c, seed, eta):
     assert abs(np.linalg.norm(wt - w) / R - eta) <= 1e-12
     cos = float(np.sum(w1 * wt)) / (np.linalg.norm(w1) * np.linalg.norm(wt))
     assert abs(cos - 1.0) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Direct pins of the remaining helpers.
+
+def test_fro_and_radius_on_integer_triples():
+    """Frobenius norms of integer matrices with known integer norms
+    (3-4-12-84 chains: 3^2+4^2 = 5^2, 5^2+12^2 = 13^2, 13^2+84^2 = 85^2)."""
+    assert om.fro(np.array([[3.0, 4.0]])) == 5.0
+    assert om.fro(np.array([[3.0, 4.0], [12.0, 0.0]])) == 13.0
+    assert om.radius(np.array([[3.0, 4.0, 12.0], [84.0, 0.0, 0.0]])) == 85.0
+    assert om.fro(np.zeros((4, 5))) == 0.0
+
+
+def test_momentum_and_nesterov_input_on_scalars():
+    """Heavy-ball momentum with beta = 1/2 on a 1 x 1 matrix: gradients 4, 2, 8
+    give M = 4, 4, 10; the Nesterov input after the last is G + beta M = 13,
+    the plain input M = 10."""
+    m = np.zeros((1, 1))
+    for g, want in ((4.0, 4.0), (2.0, 4.0), (8.0, 10.0)):
+        m = om.momentum_update(m, np.array([[g]]), 0.5)
+        assert m[0, 0] == want
+    g = np.array([[8.0]])
+    assert om.ns_input(m, g, 0.5, True)[0, 0] == 13.0
+    assert om.ns_input(m, g, 0.5, False)[0, 0] == 10.0
+
+
+def test_closed_form_angle_matches_the_turned_angle():
+    """For actual Hyperball steps the closed-form angle equals the angle
+    between W_t and W_{t+1} measured as acos(<W_t, W_{t+1}> / R^2), and the
+    chord angle; at c = 0 it is atan(eta), at c = 1 (moving straight to the
+    centre, eta < 1) it is zero."""
+    rng = np.random.default_rng(11)
+    for eta in (1e-3, 0.02, 0.3):
+        w = rng.standard_normal((20, 30))
+        R = float(np.linalg.norm(w))
+        u = rng.standard_normal((20, 30))
+        w1, d = om.hyperball_update(w, u, eta, R)
+        c = float(np.sum(w * u)) / (np.linalg.norm(u) * R)
+        th = om.closed_form_angle(eta, c)
+        measured = math.acos(max(-1.0, min(1.0, float(np.sum(w * w1)) / R ** 2)))
+        assert abs(th - measured) <= 1e-9
+        assert abs(om.chord_angle(w, w1, R) - measured) <= 1e-9
+    assert abs(om.closed_form_angle(0.1, 0.0) - math.atan(0.1)) <= 1e-15
+    assert om.closed_form_angle(0.5, 1.0) == 0.0
+
+
+def test_trajectory_zero_gradients_keep_the_projection():
+    """Zero gradients for several steps: M stays 0, u = 0, and W stays the
+    projection R W_0 / ||W_0|| of its start (here already on the sphere, so
+    W_t = W_0 to rounding) with ||W_t|| = R after every step."""
+    rng = np.random.default_rng(12)
+    w0 = rng.standard_normal((6, 9))
+    st = oracle.OracleMatrixState.from_arrays(w0)
+    grads = [[np.zeros((6, 9))] for _ in range(4)]
+    out = om.muonh_trajectory([st], grads, [0.05, 0.04, 0.03, 0.02])
+    assert len(out) == 4
+    for us, _, _ in out:
+        assert not np.any(us[0])
+    assert not np.any(st.m)
+    assert abs(np.linalg.norm(st.w) / st.R - 1.0) <= 1e-15
+    assert np.allclose(st.w, w0, rtol=0, atol=1e-14)
+
+
+def test_adamw_first_step_direction_is_the_sign_up_to_eps():
+    """g/(|g| + eps): exactly +-1/(1 + eps/|g|), i.e. the sign of g for |g| >> eps,
+    0 for g = 0, and half the sign at |g| = eps."""
+    from oracle import adamw as oa
+    g = np.array([3.0, -2.0, 0.0, 1e-8, -1e-8])
+    d = oa.first_step_direction(g, 1e-8)
+    assert d[0] == 3.0 / (3.0 + 1e-8) and d[1] == -2.0 / (2.0 + 1e-8) and d[2] == 0.0
+    assert d[3] == 0.5 and d[4] == -0.5
