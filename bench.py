@@ -72,11 +72,18 @@ KERNEL_SOURCES = ("gemm.hip", "device_util.h", "internal.h")
 
 
 def kernel_source_sha() -> str:
+    """SHA-256 of the GEMM sources with comments and blank lines removed, so
+    the recorded traffic stays tied to the code it was measured on."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "pretraining_optimizer_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "pretraining_optimizer_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [l.rstrip() for l in text.splitlines() if l.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()
 
 

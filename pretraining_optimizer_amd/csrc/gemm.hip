@@ -235,9 +235,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   // lines; of a K-major Q operand it owns rows (i*8 + t/32) and chunk t%32
   // (2 whole 512-byte row segments per instruction).  Stage s is loaded into
   // one of two register sets during stage s-3 (P half in sub-step 1, Q half
-  // in sub-step 2; for bf16 B'X spread over sub-steps 0-1 and 2-3), written to LDS slot s%2 during stage s-1 (P in sub-step
-  // 0, Q in sub-step 1) and published by the barrier that stage s-1 places
-  // before its last sub-step.
+  // in sub-step 2; for bf16 B'X spread over sub-steps 0-1 and 2-3), written
+  // to LDS slot s%2 during stage s-1 (P in sub-step 0, Q in sub-step 1) and
+  // published by the barrier that stage s-1 places before its last sub-step.
   static_assert(kSubsteps == 4, "the stage schedule below assumes 4 sub-steps");
   constexpr int kLd = kOperandBytes / 16 / kGemmThreads;   // 8 loads per operand
   const int srow = tid >> 3, schunk = tid & 7;
