@@ -12,7 +12,7 @@ the untied Qwen3-1.7B model) is timed separately and reported beside it.
 
 Prints ONE JSON line on stdout; a human-readable breakdown goes to stderr.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--graph]
 """
 
 from __future__ import annotations
@@ -185,6 +185,9 @@ def main():
     ap.add_argument("--grad-sets", type=int, default=4)
     ap.add_argument("--no-adamw", action="store_true",
                     help="skip timing the AdamW step of the non-MuonH parameters")
+    ap.add_argument("--graph", action="store_true",
+                    help="time steps replayed from a recorded HIP graph (muonh_step_graph); "
+                         "the per-kernel breakdown then comes from a second, eager timed run")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="also run one plain device-to-device copy of BYTES (for counter calibration)")
     args = ap.parse_args()
@@ -238,18 +241,33 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    opt.set_timing(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(args.steps):
-        kk = args.warmup + k
-        opt.step(pool[kk % nsets], wl.eta(kk % wl.steps), step=kk)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    def timed_run(graph: bool) -> float:
+        """Seconds for args.steps steps (eager runs record per-kernel events)."""
+        if not graph:
+            opt.set_timing(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            kk = args.warmup + k
+            opt.step(pool[kk % nsets], wl.eta(kk % wl.steps), step=kk, graph=graph)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    eager_ms = None
+    if args.graph:
+        for k in range(args.warmup):
+            opt.step(pool[k % nsets], wl.eta(k % wl.steps), step=k, graph=True)
+        torch.cuda.synchronize()
+        dt = timed_run(True)
+        log(f"graph steps: {dt * 1e3 / args.steps:.3f} ms/step")
+        eager_ms = timed_run(False) * 1e3 / args.steps
+        log(f"eager steps (per-kernel events on): {eager_ms:.3f} ms/step")
+    else:
+        dt = timed_run(False)
     phases, nt = opt.timing()
     opt.set_timing(False)
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    steps_per_s = args.steps / (t1 - t0)
+    ms_per_step = dt * 1e3 / args.steps
+    steps_per_s = args.steps / dt
     stats = opt.stats()
     R = opt.radii()
     norm_dev = max(abs(torch.linalg.vector_norm(w.double()).item() / R[i] - 1.0)
@@ -320,6 +338,8 @@ def main():
         "ns_dense_tflop_per_step": info.ns_dense_flops / 1e12,
         "elementwise_gbs": el_gbs, "elementwise_frac_of_hbm": el_gbs / PEAK_HBM_GBS,
         "elementwise_alg18_gbs": alg_gbs,
+        "step_path": "recorded HIP graph" if args.graph else "eager launches",
+        "eager_ms_per_step": eager_ms,
         "kernels": kern, "phase_ms_per_step": per_step, "timed_steps_events": nt,
         "norm_invariant_max_dev": norm_dev,
         "adamw_group": adamw,

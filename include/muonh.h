@@ -151,6 +151,20 @@ int muonh_init(muonh_handle** h, const muonh_matrix_desc* mats, int32_t n,
 int muonh_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
                const muonh_step_args* args, void* stream);
 
+/* The same step as muonh_step (same arguments, same arithmetic: results are
+ * bitwise equal), for callers whose steps are bound by launch overhead.  The
+ * first call records the step's kernel launches into a HIP graph, on a
+ * stream the handle owns; every call then enqueues on `stream` one small
+ * kernel that stores this call's per-matrix step sizes
+ * elr * elr_scale[i] (fp64) in the workspace, and one launch of the recorded
+ * graph.  Pointer changes and elr / elr_scale are taken from each call as in
+ * muonh_step; nothing needs recording again.  Returns MUONH_ESTATE when
+ * per-phase timing is on or MUONH_DEBUG_SYNC is set (use muonh_step then).
+ * Not for use while the caller is itself capturing `stream`.  The graph is
+ * released by muonh_destroy.                                                */
+int muonh_step_graph(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
+                     const muonh_step_args* args, void* stream);
+
 /* Synchronise the handle's last stream, then copy the n radii to host. */
 int muonh_get_radii(muonh_handle* h, float* out, int32_t n);
 

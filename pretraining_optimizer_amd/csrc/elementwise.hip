@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64) void finalize_norm_kernel(const MatGeom* __rest
 __global__ __launch_bounds__(64) void finalize_update_kernel(
     const MatGeom* __restrict__ geo, const double* __restrict__ partials,
     MatScalars* __restrict__ scal, muonh_stats* __restrict__ stats,
-    const float* __restrict__ elr_scale, ElemParams prm) {
+    const float* __restrict__ elr_scale, const double* __restrict__ eta_dev, ElemParams prm) {
   const int mat = blockIdx.x;
   const MatGeom& g = geo[mat];
   // per-(tile, wavefront) partials of the last B'X launch, in slot order
@@ -202,7 +202,8 @@ __global__ __launch_bounds__(64) void finalize_update_kernel(
   const double ww = ordered_sum(p + 2, g.nparts, 3);
   if (threadIdx.x != 0) return;
   const double R = scal[mat].R;
-  const double eta = (double)prm.elr * (elr_scale ? (double)elr_scale[mat] : 1.0);
+  const double eta = eta_dev ? eta_dev[mat]
+                             : (double)prm.elr * (elr_scale ? (double)elr_scale[mat] : 1.0);
   const double un = sqrt(uu), wn = sqrt(ww);
   double k1, k2, wt_norm, elr, inner, angle = 0.0;
   // u^ = u / ||u||; an all-zero u gives u^ = 0 (NaN still propagates: NaN != 0).
@@ -244,6 +245,15 @@ __global__ __launch_bounds__(64) void finalize_update_kernel(
                   isfinite(inner));
   s.reserved = 0;
   stats[mat] = s;
+}
+
+// The per-matrix step size eta_i = elr * elr_scale[i] in fp64 (the same
+// product the finaliser forms from its arguments), written to device memory
+// so that a recorded step reads this call's learning rate.
+__global__ __launch_bounds__(256) void set_eta_kernel(int32_t nmat, const float* __restrict__ elr_scale,
+                                                      float elr, double* __restrict__ eta) {
+  for (int32_t i = threadIdx.x; i < nmat; i += blockDim.x)
+    eta[i] = (double)elr * (elr_scale ? (double)elr_scale[i] : 1.0);
 }
 
 template <typename T>
@@ -431,9 +441,15 @@ hipError_t launch_finalize_norm(int32_t nmat, const MatGeom* geo, const double* 
 
 hipError_t launch_finalize_update(int32_t nmat, const MatGeom* geo, const double* partials,
                                   MatScalars* scal, muonh_stats* stats, const float* elr_scale,
-                                  ElemParams prm, hipStream_t st) {
+                                  const double* eta_dev, ElemParams prm, hipStream_t st) {
   hipLaunchKernelGGL(finalize_update_kernel, dim3(nmat), dim3(64), 0, st, geo, partials, scal,
-                     stats, elr_scale, prm);
+                     stats, elr_scale, eta_dev, prm);
+  return hipGetLastError();
+}
+
+hipError_t launch_set_eta(int32_t nmat, const float* elr_scale, float elr, double* eta,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(set_eta_kernel, dim3(1), dim3(256), 0, st, nmat, elr_scale, elr, eta);
   return hipGetLastError();
 }
 

@@ -128,9 +128,15 @@ hipError_t launch_finalize_norm(int32_t nmat, const MatGeom* geo, const double* 
                                 MatScalars* scal, float eps, hipStream_t st);
 
 
+// eta_dev (nullable): per-matrix step sizes in device memory; when given,
+// prm.elr and elr_scale are not read.
 hipError_t launch_finalize_update(int32_t nmat, const MatGeom* geo, const double* partials,
                                   MatScalars* scal, muonh_stats* stats, const float* elr_scale,
-                                  ElemParams prm, hipStream_t st);
+                                  const double* eta_dev, ElemParams prm, hipStream_t st);
+
+// eta[i] = elr * (elr_scale ? elr_scale[i] : 1) in fp64, one workgroup.
+hipError_t launch_set_eta(int32_t nmat, const float* elr_scale, float elr, double* eta,
+                          hipStream_t st);
 
 hipError_t launch_update(int bf16, const Chunk* chunks, int64_t nchunks, const MatGeom* geo,
                          const MatPtrs* ptrs, const MatScalars* scal, hipStream_t st);

@@ -76,7 +76,7 @@ struct Plan {
   int n_buckets = 0;
   double ns_dense = 0, ns_exec = 0, elem_bytes = 0;
   // workspace layout (byte offsets)
-  size_t off_geo, off_ptrs, off_scal, off_stats, off_need, off_elr;
+  size_t off_geo, off_ptrs, off_scal, off_stats, off_need, off_elr, off_eta;
   size_t off_mom_tiles, off_chunks, off_tiles[3];
   size_t off_probs_gram[2], off_probs_poly, off_probs_apply[2];
   size_t off_part_mom, off_part_radius, off_part_upd;
@@ -274,6 +274,7 @@ int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& op
   P.off_stats = take(sizeof(muonh_stats) * n);
   P.off_need = take(sizeof(int32_t) * n);
   P.off_elr = take(sizeof(float) * n);
+  P.off_eta = take(sizeof(double) * n);
   P.off_mom_tiles = take(sizeof(MomTile) * P.mom_tiles.size());
   P.off_chunks = take(sizeof(Chunk) * P.chunks.size());
   for (int k = 0; k < 3; ++k) P.off_tiles[k] = take(sizeof(GemmTile) * std::max<size_t>(1, P.tiles[k].size()));
@@ -335,6 +336,10 @@ struct muonh_handle {
   // MUONH_DEBUG_SYNC=1: synchronise after every launch and report which
   // kernel failed (slow; for attributing device faults).
   bool debug_sync = false;
+  // Recorded step for muonh_step_graph (made on its first call).
+  hipStream_t cap_stream = nullptr;
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t graph_exec = nullptr;
 
   template <typename T> T* at(size_t off) { return reinterpret_cast<T*>(ws + off); }
 };
@@ -642,15 +647,20 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
   return MUONH_OK;
 }
 
-int muonh_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
-               const muonh_step_args* args, void* stream) {
+namespace {
+
+// Checks shared by both step entry points, then the uploads the step reads
+// from device memory: the pointer table (only when the caller's pointers
+// changed) and the per-matrix LR factors.  *scale_dev receives the device
+// copy of elr_scale, or NULL.
+int prepare_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
+                 const muonh_step_args* args, hipStream_t st, const float** scale_dev) {
   if (!h || !args) return fail(MUONH_EINVAL, "null argument");
   int rc = check_same_list(h, mats, n);
   if (rc) return rc;
   if ((rc = check_pointers(mats, n, true))) return rc;
   if (!std::isfinite(args->elr)) return fail(MUONH_EINVAL, "elr is not finite");
   const Plan& pl = h->plan;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));
   if (dev != h->device) return fail(MUONH_EINVAL, "current device differs from the one at init");
@@ -668,22 +678,31 @@ int muonh_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
     h->ptrs_valid = true;
     uploaded = true;
   }
-  const float* elr_scale_dev = nullptr;
+  *scale_dev = nullptr;
   if (args->elr_scale) {
     for (int32_t i = 0; i < n; ++i)
       if (!std::isfinite(args->elr_scale[i])) return fail(MUONH_EINVAL, "elr_scale has a non-finite entry");
     if ((rc = upload_async(h, h->ws + pl.off_elr, args->elr_scale, sizeof(float) * n,
                            align_up(sizeof(MatPtrs) * n, kAlign), st)))
       return rc;
-    elr_scale_dev = h->at<float>(pl.off_elr);
+    *scale_dev = h->at<float>(pl.off_elr);
     uploaded = true;
   }
   if (uploaded) {
     HIP_TRY(hipEventRecord(h->upload_done, st));
     h->upload_pending = true;
   }
+  return MUONH_OK;
+}
 
+// Enqueues the launches of one step on `st`.  The step size is prm.elr times
+// scale_dev[i], or, when eta_dev is given, eta_dev[i] from device memory.
+int enqueue_step(muonh_handle* h, hipStream_t st, const ElemParams& prm, const float* scale_dev,
+                 const double* eta_dev) {
+  const Plan& pl = h->plan;
+  const int32_t n = pl.n;
   const int S = pl.opt.ns_steps;
+  int rc;
   if (h->timing) {
     const int k = h->ev_next;
     if ((rc = fold_events(h, k))) return rc;   // the set about to be reused
@@ -697,8 +716,6 @@ int muonh_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
     h->ev_next = (k + 1) % muonh_handle::kRing;
   }
   const int bf = pl.bf16 ? 1 : 0;
-  ElemParams prm{pl.opt.beta, pl.opt.nesterov, pl.opt.ns_eps, pl.opt.mode, pl.opt.weight_decay,
-                 args->elr};
   auto* geo = h->at<MatGeom>(pl.off_geo);
   auto* dptrs = h->at<MatPtrs>(pl.off_ptrs);
   auto* scal = h->at<MatScalars>(pl.off_scal);
@@ -734,14 +751,83 @@ int muonh_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
     if ((rc = record(h, evi++, st))) return rc;
   }
   // <W,u>, ||u||^2 and ||W||^2 were reduced per tile by the last B'X launch.
-  LAUNCH(launch_finalize_update(n, geo, part_upd, scal,
-                                h->at<muonh_stats>(pl.off_stats), elr_scale_dev, prm, st));
+  LAUNCH(launch_finalize_update(n, geo, part_upd, scal, h->at<muonh_stats>(pl.off_stats),
+                                scale_dev, eta_dev, prm, st));
   if ((rc = record(h, evi++, st))) return rc;
   LAUNCH(launch_update(bf, h->at<Chunk>(pl.off_chunks), (int64_t)pl.chunks.size(), geo, dptrs,
                        scal, st));
   if ((rc = record(h, evi++, st))) return rc;
 #undef LAUNCH
   if (h->timing) h->ev_pending[h->ev_cur] = true;
+  return MUONH_OK;
+}
+
+ElemParams step_params(const Plan& pl, float elr) {
+  return ElemParams{pl.opt.beta, pl.opt.nesterov, pl.opt.ns_eps, pl.opt.mode, pl.opt.weight_decay,
+                    elr};
+}
+
+void drop_graph(muonh_handle* h) {
+  if (h->graph_exec) (void)hipGraphExecDestroy(h->graph_exec);
+  if (h->graph) (void)hipGraphDestroy(h->graph);
+  h->graph_exec = nullptr;
+  h->graph = nullptr;
+}
+
+}  // namespace
+
+int muonh_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
+               const muonh_step_args* args, void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const float* scale_dev = nullptr;
+  int rc = prepare_step(h, mats, n, args, st, &scale_dev);
+  if (rc) return rc;
+  if ((rc = enqueue_step(h, st, step_params(h->plan, args->elr), scale_dev, nullptr))) return rc;
+  h->last_stream = st;
+  h->steps_done++;
+  return MUONH_OK;
+}
+
+int muonh_step_graph(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
+                     const muonh_step_args* args, void* stream) {
+  if (h && h->timing) return fail(MUONH_ESTATE, "per-phase timing is on: use muonh_step");
+  if (h && h->debug_sync) return fail(MUONH_ESTATE, "MUONH_DEBUG_SYNC is set: use muonh_step");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const float* scale_dev = nullptr;
+  int rc = prepare_step(h, mats, n, args, st, &scale_dev);
+  if (rc) return rc;
+  const Plan& pl = h->plan;
+  double* eta = h->at<double>(pl.off_eta);
+  {
+    const hipError_t e = launch_set_eta(n, scale_dev, args->elr, eta, st);
+    if (e != hipSuccess) return fail(MUONH_EHIP, std::string("launch_set_eta: ") + hipGetErrorString(e));
+  }
+  if (!h->graph_exec) {
+    // Record the launches once on a private stream; every argument they take
+    // is fixed by the plan (tables, workspace addresses, the pointer table's
+    // address), and the step size comes from `eta`.
+    if (!h->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
+    HIP_TRY(hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
+    rc = enqueue_step(h, h->cap_stream, step_params(pl, 0.0f), nullptr, eta);
+    hipGraph_t g = nullptr;
+    const hipError_t e_end = hipStreamEndCapture(h->cap_stream, &g);
+    if (rc) {
+      if (g) (void)hipGraphDestroy(g);
+      return rc;
+    }
+    if (e_end != hipSuccess || !g) {
+      if (g) (void)hipGraphDestroy(g);
+      return fail(MUONH_EHIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e_end));
+    }
+    h->graph = g;
+    const hipError_t e_inst = hipGraphInstantiate(&h->graph_exec, g, nullptr, nullptr, 0);
+    if (e_inst != hipSuccess) {
+      h->graph_exec = nullptr;
+      drop_graph(h);
+      return fail(MUONH_EHIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e_inst));
+    }
+  }
+  HIP_TRY(hipGraphLaunch(h->graph_exec, st));
   h->last_stream = st;
   h->steps_done++;
   return MUONH_OK;
@@ -810,6 +896,8 @@ int muonh_destroy(muonh_handle* h) {
   if (h->owns_ws && h->ws) (void)hipFree(h->ws);
   if (h->staging) (void)hipHostFree(h->staging);
   if (h->upload_done) (void)hipEventDestroy(h->upload_done);
+  drop_graph(h);
+  if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
   for (auto& set : h->ev)
     for (auto e : set) (void)hipEventDestroy(e);
   delete h;

@@ -97,6 +97,8 @@ _SIGNATURES = [
                                   ctypes.c_int32, ctypes.POINTER(muonh_options), ctypes.c_void_p]),
     ("muonh_step", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(muonh_matrix_desc), ctypes.c_int32,
                                   ctypes.POINTER(muonh_step_args), ctypes.c_void_p]),
+    ("muonh_step_graph", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(muonh_matrix_desc), ctypes.c_int32,
+                                        ctypes.POINTER(muonh_step_args), ctypes.c_void_p]),
     ("muonh_get_radii", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int32]),
     ("muonh_get_stats", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(muonh_stats), ctypes.c_int32]),
     ("muonh_copy_update", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
@@ -258,7 +260,8 @@ class MuonH:
         self._descs = descs
 
     def step(self, grads: Sequence, elr: float, elr_scale: Optional[Sequence[float]] = None,
-             step: int = 0, stream=None):
+             step: int = 0, stream=None, graph: bool = False):
+        """One step; graph=True goes through muonh_step_graph (a recorded HIP graph)."""
         if len(grads) != self.n:
             raise ValueError("one gradient per matrix is required")
         d = self._descs
@@ -278,8 +281,9 @@ class MuonH:
             scale_arr = (ctypes.c_float * self.n)(*[float(x) for x in elr_scale])
             args.elr_scale = ctypes.cast(scale_arr, ctypes.POINTER(ctypes.c_float))
         args.step = int(step)
-        _check(self._lib.muonh_step(self._h, d, self.n, ctypes.byref(args), _stream_ptr(stream)),
-               "muonh_step")
+        fn, name = ((self._lib.muonh_step_graph, "muonh_step_graph") if graph
+                    else (self._lib.muonh_step, "muonh_step"))
+        _check(fn(self._h, d, self.n, ctypes.byref(args), _stream_ptr(stream)), name)
 
     def radii(self) -> List[float]:
         out = (ctypes.c_float * self.n)()

@@ -19,7 +19,11 @@ hipError_t launch_finalize_norm(int32_t, const MatGeom*, const double*, MatScala
   return hipErrorNoDevice;
 }
 hipError_t launch_finalize_update(int32_t, const MatGeom*, const double*, MatScalars*,
-                                  muonh_stats*, const float*, ElemParams, hipStream_t) {
+                                  muonh_stats*, const float*, const double*, ElemParams,
+                                  hipStream_t) {
+  return hipErrorNoDevice;
+}
+hipError_t launch_set_eta(int32_t, const float*, float, double*, hipStream_t) {
   return hipErrorNoDevice;
 }
 hipError_t launch_update(int, const Chunk*, int64_t, const MatGeom*, const MatPtrs*,

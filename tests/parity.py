@@ -50,8 +50,10 @@ def run_parity(shapes: Sequence, make_w: Callable[[int], torch.Tensor],
                make_g: Callable[[int, int], torch.Tensor], etas: Sequence[float],
                check: Sequence[int], ns: str = "bf16", oracle_opts: Optional[oracle.OracleOptions] = None,
                mode: int = pm.MUONH_MODE_HYPERBALL, weight_decay: float = 0.0,
-               elr_scale: Optional[Sequence[float]] = None, radii=None, **lib_opts) -> List[StepReport]:
-    """make_w(i) -> fp32 CUDA tensor, make_g(step, i) -> CUDA gradient."""
+               elr_scale: Optional[Sequence[float]] = None, radii=None, graph: bool = False,
+               **lib_opts) -> List[StepReport]:
+    """make_w(i) -> fp32 CUDA tensor, make_g(step, i) -> CUDA gradient.
+    graph=True takes every step through the recorded-graph entry point."""
     dev = torch.device("cuda")
     oo = oracle_opts or oracle.OracleOptions()
     ws = [make_w(i).to(dev).contiguous() for i in range(len(shapes))]
@@ -72,7 +74,7 @@ def run_parity(shapes: Sequence, make_w: Callable[[int], torch.Tensor],
     reports = []
     for k, eta in enumerate(etas):
         gs = [make_g(k, i).to(dev).contiguous() for i in range(len(shapes))]
-        opt.step(gs, eta, elr_scale=elr_scale, step=k)
+        opt.step(gs, eta, elr_scale=elr_scale, step=k, graph=graph)
         us = {i: inputs.to_numpy64(opt.copy_update(i)) for i in check}
         torch.cuda.synchronize()
         stats = opt.stats()
