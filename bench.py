@@ -139,6 +139,37 @@ def cpu_baseline(wl, ws_dev, grads_dev, eta, layer_mats: int):
             "seconds_sample": dt, "host_cpus": os.cpu_count()}
 
 
+def hbm_ceiling(n_elems: int, dev) -> dict:
+    """Plain streaming rates of this GPU, measured with PyTorch's own kernels
+    on three fp32 buffers of n_elems elements: read-only (sum), write-only (fill),
+    copy, and a read-2/write-1 add.  Reads and writes do not stream at the
+    same rate, so a kernel's fraction of the 8 TB/s peak is bounded by its
+    read/write mix."""
+    import torch
+    a = torch.ones(n_elems, dtype=torch.float32, device=dev)
+    b = torch.ones_like(a)
+    c = torch.empty_like(a)
+    ops = {"read_sum": (lambda: a.sum(), 4),
+           "write_fill": (lambda: c.fill_(1.5), 4),
+           "copy": (lambda: c.copy_(a), 8),
+           "add_read2_write1": (lambda: torch.add(a, b, out=c), 12)}
+    out = {}
+    for name, (fn, bpe) in ops.items():
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            fn()
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        out[name + "_gbs"] = bpe * n_elems / (ms * 1e-3) / 1e9
+    del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_adamw(steps: int, warmup: int, dev):
     """The AdamW step of the parameters MuonH does not wrap (untied Qwen3-1.7B
     embedding, LM head and normalisation weights), timed with HIP events on
@@ -185,6 +216,8 @@ def main():
     ap.add_argument("--grad-sets", type=int, default=4)
     ap.add_argument("--no-adamw", action="store_true",
                     help="skip timing the AdamW step of the non-MuonH parameters")
+    ap.add_argument("--no-hbm-ceiling", action="store_true",
+                    help="skip measuring this GPU's plain streaming rates (torch read/write/copy/add)")
     ap.add_argument("--graph", action="store_true",
                     help="time steps replayed from a recorded HIP graph (muonh_step_graph); "
                          "the per-kernel breakdown then comes from a second, eager timed run")
@@ -317,6 +350,11 @@ def main():
             "ms_per_launch": kern[dom]["ms_per_launch"]}
 
     adamw = None if args.no_adamw else time_adamw(args.steps, args.warmup, dev)
+    ceiling = None
+    if not args.no_hbm_ceiling:
+        ceiling = hbm_ceiling(max(params, 1 << 28), dev)
+        log("plain streaming on this GPU (torch, fp32, one buffer of the workload's size): " +
+            ", ".join(f"{k} {v:.0f} GB/s" for k, v in ceiling.items()))
 
     cpu = None
     if cpu_inputs is not None:
@@ -343,6 +381,7 @@ def main():
         "kernels": kern, "phase_ms_per_step": per_step, "timed_steps_events": nt,
         "norm_invariant_max_dev": norm_dev,
         "adamw_group": adamw,
+        "hbm_streaming_ceiling": ceiling,
         "cpu_baseline": cpu,
     }
     opt.close()

@@ -116,7 +116,8 @@ typedef struct muonh_plan_info {
   int32_t n_matrices;
   int32_t n_buckets;        /* distinct padded NS shapes (m_pad x n_pad)            */
   int64_t gemm_tiles[3];    /* 256x256 output tiles per launch: XX^T, AA, BX          */
-  int64_t mom_tiles;        /* 64x64 tiles of the momentum / pack kernel             */
+  int64_t mom_tiles;        /* blocks of the momentum / pack kernel: 64x64 tiles, or
+                               1024-column row segments where X_0 is not transposed */
   int64_t flat_chunks;      /* chunks of the reduction and update kernels            */
   double  ns_dense_flops;   /* sum over matrices of steps*(4 m^2 n + 2 m^3)          */
   double  ns_exec_flops;    /* MFMA FLOP issued per step (padding + symmetric tiles) */

@@ -147,6 +147,51 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, const MatGeom& g
   if (tid == 0) partials[blockIdx.x] = v[0];
 }
 
+// momentum + pack for a matrix whose X_0 keeps M's orientation and has no
+// transposed copy: columns [tc * kMomRowSeg, +kMomRowSeg) of row tr of the
+// padded grid, 4 consecutive columns per thread.  Short blocks over
+// consecutive addresses stream faster than 64 x 64 tiles (each of which
+// touches 64 rows); pad rows and columns of X_0 are written as zeros.
+template <typename T, typename G>
+__device__ __forceinline__ void momentum_row(const MomTile& t, const MatGeom& g, const MatPtrs& p,
+                                             double* partials, const ElemParams& prm,
+                                             double (*red)[4]) {
+  static_assert(kMomRowSeg == kElemThreads * 4, "one 4-column group per thread");
+  const int64_t row = t.tr;
+  const int64_t col = (int64_t)t.tc * kMomRowSeg + threadIdx.x * 4;
+  T* D = reinterpret_cast<T*>(g.X[0]);
+  const int64_t ldD = g.c_pad + g.ld_skew;
+  const float beta = prm.beta;
+  float ss = 0.0f;
+  if (col < g.c_pad) {   // c_pad is a multiple of 4
+    f32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (row < g.rows) {
+      const int64_t off = row * g.cols + col;
+      if ((g.cols & 3) == 0 && col + 4 <= g.cols) {
+        const f32x4_t gv = GradLoad<G>::load4(p.g, off);
+        const f32x4_t m = beta * Vec4<float>::load_nt(p.m + off) + gv;
+        Vec4<float>::store_nt(p.m + off, m);
+        y = prm.nesterov ? gv + beta * m : m;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (col + e < g.cols) {
+            const float gs = GradLoad<G>::load1(p.g, off + e);
+            const float ms = beta * p.m[off + e] + gs;
+            p.m[off + e] = ms;
+            y[e] = prm.nesterov ? gs + beta * ms : ms;
+          }
+        }
+      }
+    }
+    ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
+    Vec4<T>::store(D + row * ldD + col, y);
+  }
+  double v[1] = {(double)ss};
+  block_sum<1>(v, red);
+  if (threadIdx.x == 0) partials[blockIdx.x] = v[0];
+}
+
 template <typename T>
 __global__ __launch_bounds__(kElemThreads) void momentum_kernel(const MomTile* __restrict__ tiles,
                                                                 const MatGeom* __restrict__ geo,
@@ -158,10 +203,16 @@ __global__ __launch_bounds__(kElemThreads) void momentum_kernel(const MomTile* _
   const MomTile t = tiles[blockIdx.x];
   const MatGeom& g = geo[t.mat];
   const MatPtrs p = ptrs[t.mat];
-  if (g.g_bf16)
+  if (t.kind == 1) {
+    if (g.g_bf16)
+      momentum_row<T, uint16_t>(t, g, p, partials, prm, red);
+    else
+      momentum_row<T, float>(t, g, p, partials, prm, red);
+  } else if (g.g_bf16) {
     momentum_tile<T, uint16_t>(t, g, p, partials, prm, tile, red);
-  else
+  } else {
     momentum_tile<T, float>(t, g, p, partials, prm, tile, red);
+  }
 }
 
 // Sum of a matrix's block partials in block order, one wavefront per matrix:
@@ -256,42 +307,40 @@ __global__ __launch_bounds__(256) void set_eta_kernel(int32_t nmat, const float*
     eta[i] = (double)elr * (elr_scale ? (double)elr_scale[i] : 1.0);
 }
 
+// The flat streaming kernels (update, AdamW) run one block per slice of
+// kSlice elements, kSlicesPerChunk blocks per chunk, each thread one 16-byte
+// vector of every stream: many short blocks, dispatched in order, keep the
+// addresses in flight within a narrow ascending window, which streams faster
+// on HBM3E than long per-block loops (measured on MI355X: 6.5 TB/s against
+// 5.3 TB/s for the same read/write mix).
+constexpr int kSlice = kElemThreads * 4;
+constexpr int kSlicesPerChunk = kChunk / kSlice;
+static_assert(kChunk % kSlice == 0, "a chunk is a whole number of slices");
+
 template <typename T>
 __global__ __launch_bounds__(kElemThreads) void update_kernel(const Chunk* __restrict__ chunks,
                                                               const MatGeom* __restrict__ geo,
                                                               const MatPtrs* __restrict__ ptrs,
                                                               const MatScalars* __restrict__ scal) {
-  const Chunk c = chunks[blockIdx.x];
+  const Chunk c = chunks[blockIdx.x / kSlicesPerChunk];
+  const int s0 = (int)(blockIdx.x % kSlicesPerChunk) * kSlice;
+  if (s0 >= c.len) return;
+  const int len = min(kSlice, c.len - s0);
   const MatGeom& g = geo[c.mat];
-  float* W = ptrs[c.mat].w + c.start;
-  const T* U = reinterpret_cast<const T*>(g.U) + c.start;
+  float* W = ptrs[c.mat].w + c.start + s0;
+  const T* U = reinterpret_cast<const T*>(g.U) + c.start + s0;
   const float k1 = scal[c.mat].k1, k2 = scal[c.mat].k2;
-  const int tid = threadIdx.x;
-  const int n4 = c.len & ~3;
-  // Batches of 4 x 4 elements per thread: every load of a batch is issued
-  // before its stores (W is written in place, so the compiler may not hoist
-  // loads across them itself).
-  constexpr int kStep = kElemThreads * 4;
-  int i = tid * 4;
-  for (; i + 3 * kStep < n4; i += 4 * kStep) {
-    f32x4_t w[4], u[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      w[k] = Vec4<float>::load_nt(W + i + k * kStep);
-      u[k] = Vec4<T>::load_nt(U + i + k * kStep);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) Vec4<float>::store_nt(W + i + k * kStep, k1 * w[k] - k2 * u[k]);
-  }
-  for (; i < n4; i += kStep) {
+  const int i = threadIdx.x * 4;
+  if (i + 4 <= len) {
     const f32x4_t w = Vec4<float>::load_nt(W + i);
     const f32x4_t u = Vec4<T>::load_nt(U + i);
     Vec4<float>::store_nt(W + i, k1 * w - k2 * u);
-  }
-  for (int j = n4 + tid; j < c.len; j += kElemThreads) {
-    float u;
-    if constexpr (sizeof(T) == 2) u = bf16_to_f32(U[j]); else u = U[j];
-    W[j] = k1 * W[j] - k2 * u;
+  } else {
+    for (int j = i; j < len; ++j) {
+      float u;
+      if constexpr (sizeof(T) == 2) u = bf16_to_f32(U[j]); else u = U[j];
+      W[j] = k1 * W[j] - k2 * u;
+    }
   }
 }
 
@@ -357,36 +406,15 @@ __device__ __forceinline__ void adamw4(f32x4_t& w, f32x4_t& m, f32x4_t& v, const
 }
 
 template <typename G>
-__device__ __forceinline__ void adamw_chunk(const Chunk& c, const AdamwPtrs& q,
+__device__ __forceinline__ void adamw_slice(const Chunk& c, int s0, const AdamwPtrs& q,
                                             const AdamwParams& p) {
-  float* W = q.w + c.start;
-  float* Mm = q.m + c.start;
-  float* V = q.v + c.start;
-  const G* Gp = reinterpret_cast<const G*>(q.g) + c.start;
-  const int tid = threadIdx.x;
-  const int n4 = c.len & ~3;
-  constexpr int kStep = kElemThreads * 4;
-  // Batches of 2 x 4 elements per thread, every load issued before the
-  // stores (W, m, v are written in place).
-  int i = tid * 4;
-  for (; i + kStep < n4; i += 2 * kStep) {
-    f32x4_t w[2], m[2], v[2], g[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      w[k] = Vec4<float>::load_nt(W + i + k * kStep);
-      m[k] = Vec4<float>::load_nt(Mm + i + k * kStep);
-      v[k] = Vec4<float>::load_nt(V + i + k * kStep);
-      g[k] = Vec4<G>::load_nt(Gp + i + k * kStep);
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      adamw4(w[k], m[k], v[k], g[k], p);
-      Vec4<float>::store_nt(W + i + k * kStep, w[k]);
-      Vec4<float>::store_nt(Mm + i + k * kStep, m[k]);
-      Vec4<float>::store_nt(V + i + k * kStep, v[k]);
-    }
-  }
-  for (; i < n4; i += kStep) {
+  const int len = min(kSlice, c.len - s0);
+  float* W = q.w + c.start + s0;
+  float* Mm = q.m + c.start + s0;
+  float* V = q.v + c.start + s0;
+  const G* Gp = reinterpret_cast<const G*>(q.g) + c.start + s0;
+  const int i = threadIdx.x * 4;
+  if (i + 4 <= len) {
     f32x4_t w = Vec4<float>::load_nt(W + i), m = Vec4<float>::load_nt(Mm + i);
     f32x4_t v = Vec4<float>::load_nt(V + i);
     const f32x4_t g = Vec4<G>::load_nt(Gp + i);
@@ -394,26 +422,29 @@ __device__ __forceinline__ void adamw_chunk(const Chunk& c, const AdamwPtrs& q,
     Vec4<float>::store_nt(W + i, w);
     Vec4<float>::store_nt(Mm + i, m);
     Vec4<float>::store_nt(V + i, v);
-  }
-  for (int j = n4 + tid; j < c.len; j += kElemThreads) {
-    float g;
-    if constexpr (sizeof(G) == 2) g = bf16_to_f32(Gp[j]); else g = Gp[j];
-    float m = Mm[j], v = V[j];
-    W[j] = adamw_elem(W[j], m, v, g, p);
-    Mm[j] = m;
-    V[j] = v;
+  } else {
+    for (int j = i; j < len; ++j) {
+      float g;
+      if constexpr (sizeof(G) == 2) g = bf16_to_f32(Gp[j]); else g = Gp[j];
+      float m = Mm[j], v = V[j];
+      W[j] = adamw_elem(W[j], m, v, g, p);
+      Mm[j] = m;
+      V[j] = v;
+    }
   }
 }
 
 __global__ __launch_bounds__(kElemThreads) void adamw_kernel(const Chunk* __restrict__ chunks,
                                                              const AdamwPtrs* __restrict__ ptrs,
                                                              AdamwParams prm) {
-  const Chunk c = chunks[blockIdx.x];
+  const Chunk c = chunks[blockIdx.x / kSlicesPerChunk];
+  const int s0 = (int)(blockIdx.x % kSlicesPerChunk) * kSlice;
+  if (s0 >= c.len) return;
   const AdamwPtrs q = ptrs[c.mat];
   if (q.g_bf16)
-    adamw_chunk<uint16_t>(c, q, prm);
+    adamw_slice<uint16_t>(c, s0, q, prm);
   else
-    adamw_chunk<float>(c, q, prm);
+    adamw_slice<float>(c, s0, q, prm);
 }
 
 }  // namespace
@@ -456,12 +487,13 @@ hipError_t launch_set_eta(int32_t nmat, const float* elr_scale, float elr, doubl
 hipError_t launch_update(int bf16, const Chunk* chunks, int64_t nchunks, const MatGeom* geo,
                          const MatPtrs* ptrs, const MatScalars* scal, hipStream_t st) {
   if (nchunks <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)(nchunks * kSlicesPerChunk);
   if (bf16)
-    hipLaunchKernelGGL(update_kernel<uint16_t>, dim3((unsigned)nchunks), dim3(kElemThreads), 0, st,
-                       chunks, geo, ptrs, scal);
+    hipLaunchKernelGGL(update_kernel<uint16_t>, dim3(grid), dim3(kElemThreads), 0, st, chunks,
+                       geo, ptrs, scal);
   else
-    hipLaunchKernelGGL(update_kernel<float>, dim3((unsigned)nchunks), dim3(kElemThreads), 0, st,
-                       chunks, geo, ptrs, scal);
+    hipLaunchKernelGGL(update_kernel<float>, dim3(grid), dim3(kElemThreads), 0, st, chunks, geo,
+                       ptrs, scal);
   return hipGetLastError();
 }
 
@@ -495,8 +527,8 @@ hipError_t launch_copy_update(int bf16, const void* U, int64_t count, float* dst
 hipError_t launch_adamw(const Chunk* chunks, int64_t nchunks, const AdamwPtrs* ptrs,
                         AdamwParams prm, hipStream_t st) {
   if (nchunks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)nchunks), dim3(kElemThreads), 0, st, chunks,
-                     ptrs, prm);
+  hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)(nchunks * kSlicesPerChunk)), dim3(kElemThreads),
+                     0, st, chunks, ptrs, prm);
   return hipGetLastError();
 }
 

@@ -53,11 +53,17 @@ struct GemmTile {
   int16_t tm, tn;
 };
 
+// One block of the momentum kernel.  kind 0: the 64 x 64 tile (tr, tc) of
+// the padded, original-orientation grid (the path that also writes a
+// transposed X_0); kind 1: columns [tc * 1024, tc * 1024 + 1024) of row tr
+// of that grid (matrices whose X_0 keeps M's orientation and has no
+// transposed copy).
 struct MomTile {
   int32_t mat;
-  int32_t tr, tc;  // tile coordinates in the padded, original-orientation grid
-  int32_t pad_;
+  int32_t tr, tc;
+  int32_t kind;
 };
+constexpr int kMomRowSeg = 1024;   // columns per kind-1 block
 
 struct Chunk {
   int32_t mat;

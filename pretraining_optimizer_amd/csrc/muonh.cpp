@@ -218,10 +218,19 @@ int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& op
     buckets[{m.m_pad, m.n_pad}]++;
     const int64_t r_pad = m.tall ? m.n_pad : m.m_pad, c_pad = m.tall ? m.m_pad : m.n_pad;
     m.mom_tile0 = mom_tiles;
-    m.mom_ntiles = (r_pad / kMomTile) * (c_pad / kMomTile);
-    for (int64_t tr = 0; tr < r_pad / kMomTile; ++tr)
-      for (int64_t tc = 0; tc < c_pad / kMomTile; ++tc)
-        P.mom_tiles.push_back({i, (int32_t)tr, (int32_t)tc, 0});
+    if (P.bf16 && !m.tall) {
+      // X_0 keeps M's orientation and has no transposed copy: row segments.
+      const int64_t nseg = (c_pad + kMomRowSeg - 1) / kMomRowSeg;
+      m.mom_ntiles = r_pad * nseg;
+      for (int64_t r = 0; r < r_pad; ++r)
+        for (int64_t sg = 0; sg < nseg; ++sg)
+          P.mom_tiles.push_back({i, (int32_t)r, (int32_t)sg, 1});
+    } else {
+      m.mom_ntiles = (r_pad / kMomTile) * (c_pad / kMomTile);
+      for (int64_t tr = 0; tr < r_pad / kMomTile; ++tr)
+        for (int64_t tc = 0; tc < c_pad / kMomTile; ++tc)
+          P.mom_tiles.push_back({i, (int32_t)tr, (int32_t)tc, 0});
+    }
     mom_tiles += m.mom_ntiles;
     const int64_t elems = m.rows * m.cols;
     m.chunk0 = nchunks;
