@@ -1,9 +1,12 @@
 // Fused, coalesced elementwise / reduction kernels of the MuonH step (gfx950).
 //
 // The step around the Newton-Schulz products is memory-bound streaming work:
-//   momentum_kernel : M <- beta M + G, Y = M (or G + beta M), partial ||Y||^2,
-//                     Y packed as the first iterate X_0 in BOTH layouts the
-//                     grouped GEMM reads (X and X^T), zero-padded;
+//   momentum_row_kernel / momentum_tile_kernel :
+//                     M <- beta M + G, Y = M (or G + beta M), partial ||Y||^2,
+//                     Y packed as the first iterate X_0, zero-padded, in the
+//                     layouts the grouped GEMM reads (X, and X^T in the fp32
+//                     plan): row segments where X_0 keeps M's orientation,
+//                     64 x 128 tiles through LDS where it is transposed;
 //   (<W,u>, ||u||^2, ||W||^2 are reduced per tile by the last Newton-Schulz
 //   product's epilogue, gemm.hip);
 //   update_kernel   : W <- k1 W - k2 u  (Hyperball: k1 = R/||W~||,
@@ -69,17 +72,47 @@ template <> struct GradLoad<float> {
 };
 
 // ---------------------------------------------------------------------------
-// momentum + pack.  One 64 x 64 tile of the padded, original-orientation grid
-// per block; thread (rr, cc) handles rows rr + 16q, columns cc..cc+3.
+// momentum + pack.  One 64 x 128 tile of the padded, original-orientation
+// grid per block (rows of 512 bytes of M: wider tiles stream faster, measured
+// on MI355X); thread (rr, cc) handles rows rr + 8q, columns cc..cc+3.  The
+// transposed X_0 is staged through LDS in the Newton-Schulz element type.
+
+// ||Y||^2 partial of one momentum unit: one slot per wavefront (a fixed-order
+// fp64 shuffle tree inside the wavefront; no block-wide barrier).
+__device__ __forceinline__ void write_wave_partial(double* partials, int64_t unit, float ss) {
+  const double s = wave_sum((double)ss);
+  if ((threadIdx.x & 63) == 0) partials[kMomParts * unit + (threadIdx.x >> 6)] = s;
+}
+
+template <typename T> __device__ __forceinline__ T to_elem(float v);
+template <> __device__ __forceinline__ float to_elem<float>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t to_elem<uint16_t>(float v) { return f32_to_bf16(v); }
+
+// 4 consecutive elements already in the element type.
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  st_global<f32x4_t>(p, f32x4_t{a, b, c, d});
+}
+__device__ __forceinline__ void store4(uint16_t* p, uint16_t a, uint16_t b, uint16_t c, uint16_t d) {
+  st_global<u32x2_t>(p, u32x2_t{(uint32_t)a | ((uint32_t)b << 16), (uint32_t)c | ((uint32_t)d << 16)});
+}
+
+template <typename T> struct MomLds {
+  // one padding element per row (two for 2-byte types, keeping rows 4-byte aligned)
+  static constexpr int kPitch = kMomTileC + (sizeof(T) == 2 ? 2 : 1);
+};
 
 template <typename T, typename G>
-__device__ __forceinline__ void momentum_tile(const MomTile& t, const MatGeom& g, const MatPtrs& p,
-                                              double* partials, const ElemParams& prm,
-                                              float (*tile)[kMomTile + 1], double (*red)[4]) {
+__device__ __forceinline__ void momentum_tile(const MomTile& t, int64_t unit, const MatGeom& g,
+                                              const MatPtrs& p, double* partials,
+                                              const ElemParams& prm,
+                                              T (*tile)[MomLds<T>::kPitch]) {
+  constexpr int kTpr = kMomTileC / 4;               // threads per row
+  constexpr int kRpp = kElemThreads / kTpr;         // rows per pass
+  constexpr int kPasses = kMomTileR / kRpp;
   const int tid = threadIdx.x;
-  const int cc = (tid & 15) * 4;
-  const int rr = tid >> 4;
-  const int64_t r0 = (int64_t)t.tr * kMomTile, c0 = (int64_t)t.tc * kMomTile;
+  const int cc = (tid % kTpr) * 4;
+  const int rr = tid / kTpr;
+  const int64_t r0 = (int64_t)t.tr * kMomTileR, c0 = (int64_t)t.tc * kMomTileC;
   // X_0 in M's orientation (D) and transposed (Tr); the bf16 plan keeps only
   // X (no X^T), so one of the two is absent.
   T* D = reinterpret_cast<T*>(g.tall ? g.XT[0] : g.X[0]);
@@ -89,62 +122,69 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, const MatGeom& g
   const float beta = prm.beta;
   float ss = 0.0f;
 
-  // All loads of the thread's four rows are issued before the first store
-  // (M is written in place, so the compiler may not hoist them itself).
-  f32x4_t gv[4], mv[4];
-  bool full[4];
+  // The tile is done as two halves of kHalf passes; all loads of a half are
+  // issued before its first store (M is written in place, so the compiler
+  // may not hoist them itself).  Two halves instead of one batch of all
+  // passes keep the register count, and so the occupancy, of a 64-row tile.
+  constexpr int kHalf = kPasses / 2;
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    f32x4_t gv[kHalf], mv[kHalf];
+    bool full[kHalf];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t row = r0 + rr + 16 * q;
-    const int64_t col = c0 + cc;
-    full[q] = row < g.rows && vec_ok && col + 3 < g.cols;
-    if (full[q]) {
-      const int64_t off = row * g.cols + col;
-      gv[q] = GradLoad<G>::load4(p.g, off);
-      mv[q] = Vec4<float>::load_nt(p.m + off);
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t row = r0 + rr + 16 * q;
-    const int64_t col = c0 + cc;
-    f32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
-    const int64_t off = row * g.cols + col;
-    if (full[q]) {
-      const f32x4_t m = beta * mv[q] + gv[q];
-      Vec4<float>::store_nt(p.m + off, m);
-      y = prm.nesterov ? gv[q] + beta * m : m;
-    } else if (row < g.rows) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (col + e < g.cols) {
-          const float gs = GradLoad<G>::load1(p.g, off + e);
-          const float ms = beta * p.m[off + e] + gs;
-          p.m[off + e] = ms;
-          y[e] = prm.nesterov ? gs + beta * ms : ms;
-        }
+    for (int q = 0; q < kHalf; ++q) {
+      const int64_t row = r0 + rr + kRpp * (h * kHalf + q);
+      const int64_t col = c0 + cc;
+      full[q] = row < g.rows && vec_ok && col + 3 < g.cols;
+      if (full[q]) {
+        const int64_t off = row * g.cols + col;
+        gv[q] = GradLoad<G>::load4(p.g, off);
+        mv[q] = Vec4<float>::load_nt(p.m + off);
       }
     }
-    ss += y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
-    if (Tr)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tile[rr + 16 * q][cc + e] = y[e];
-    if (D) Vec4<T>::store(D + row * ldD + col, y);
+    for (int q = 0; q < kHalf; ++q) {
+      const int tr_ = rr + kRpp * (h * kHalf + q);   // row inside the tile
+      const int64_t row = r0 + tr_;
+      const int64_t col = c0 + cc;
+      f32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
+      const int64_t off = row * g.cols + col;
+      if (full[q]) {
+        const f32x4_t m = beta * mv[q] + gv[q];
+        Vec4<float>::store_nt(p.m + off, m);
+        y = prm.nesterov ? gv[q] + beta * m : m;
+      } else if (row < g.rows) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (col + e < g.cols) {
+            const float gs = GradLoad<G>::load1(p.g, off + e);
+            const float ms = beta * p.m[off + e] + gs;
+            p.m[off + e] = ms;
+            y[e] = prm.nesterov ? gs + beta * ms : ms;
+          }
+        }
+      }
+      ss += y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
+      if (Tr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tile[tr_][cc + e] = to_elem<T>(y[e]);
+      if (D) Vec4<T>::store(D + row * ldD + col, y);
+    }
   }
   if (Tr) {
     __syncthreads();
+    // output row oc (= tile column) holds the tile's 64 rows, 4 per thread
+    constexpr int kTpo = kMomTileR / 4;             // threads per output row
+    constexpr int kOpp = kElemThreads / kTpo;       // output rows per pass
+    const int oe = (tid % kTpo) * 4, orow = tid / kTpo;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int oc = rr + 16 * q;  // column of the source tile = row of the transposed output
-      f32x4_t y;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = tile[cc + e][oc];
-      Vec4<T>::store(Tr + (c0 + oc) * ldT + r0 + cc, y);
+    for (int q = 0; q < kMomTileC / kOpp; ++q) {
+      const int oc = orow + kOpp * q;
+      store4(Tr + (c0 + oc) * ldT + r0 + oe, tile[oe][oc], tile[oe + 1][oc], tile[oe + 2][oc],
+             tile[oe + 3][oc]);
     }
   }
-  double v[1] = {(double)ss};
-  block_sum<1>(v, red);
-  if (tid == 0) partials[blockIdx.x] = v[0];
+  write_wave_partial(partials, unit, ss);
 }
 
 // momentum + pack for a matrix whose X_0 keeps M's orientation and has no
@@ -153,21 +193,28 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, const MatGeom& g
 // consecutive addresses stream faster than 64 x 64 tiles (each of which
 // touches 64 rows); pad rows and columns of X_0 are written as zeros.
 template <typename T, typename G>
-__device__ __forceinline__ void momentum_row(const MomTile& t, const MatGeom& g, const MatPtrs& p,
-                                             double* partials, const ElemParams& prm,
-                                             double (*red)[4]) {
+__device__ __forceinline__ void momentum_row(const MomTile& t, int64_t unit, const MatGeom& g,
+                                             const MatPtrs& p, double* partials,
+                                             const ElemParams& prm) {
   static_assert(kMomRowSeg == kElemThreads * 4, "one 4-column group per thread");
+  // Every field is read before the first branch, so the scalar loads issue
+  // together (one round trip) rather than one behind each branch: with
+  // blocks this short the chain of dependent loads sets the pace.
+  const int64_t rows = g.rows, cols = g.cols;
+  const int64_t c_pad = g.c_pad, ldD = g.c_pad + g.ld_skew;
+  T* D = reinterpret_cast<T*>(g.X[0]);
+  // (an empty use in scalar registers: the compiler would otherwise sink the
+  // loads of rows and cols behind the divergent branches below)
+  asm volatile("" ::"s"(rows), "s"(cols));
   const int64_t row = t.tr;
   const int64_t col = (int64_t)t.tc * kMomRowSeg + threadIdx.x * 4;
-  T* D = reinterpret_cast<T*>(g.X[0]);
-  const int64_t ldD = g.c_pad + g.ld_skew;
   const float beta = prm.beta;
   float ss = 0.0f;
-  if (col < g.c_pad) {   // c_pad is a multiple of 4
+  if (col < c_pad) {   // c_pad is a multiple of 4
     f32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (row < g.rows) {
-      const int64_t off = row * g.cols + col;
-      if ((g.cols & 3) == 0 && col + 4 <= g.cols) {
+    if (row < rows) {
+      const int64_t off = row * cols + col;
+      if ((cols & 3) == 0 && col + 4 <= cols) {
         const f32x4_t gv = GradLoad<G>::load4(p.g, off);
         const f32x4_t m = beta * Vec4<float>::load_nt(p.m + off) + gv;
         Vec4<float>::store_nt(p.m + off, m);
@@ -175,7 +222,7 @@ __device__ __forceinline__ void momentum_row(const MomTile& t, const MatGeom& g,
       } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (col + e < g.cols) {
+          if (col + e < cols) {
             const float gs = GradLoad<G>::load1(p.g, off + e);
             const float ms = beta * p.m[off + e] + gs;
             p.m[off + e] = ms;
@@ -187,32 +234,41 @@ __device__ __forceinline__ void momentum_row(const MomTile& t, const MatGeom& g,
     ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
     Vec4<T>::store(D + row * ldD + col, y);
   }
-  double v[1] = {(double)ss};
-  block_sum<1>(v, red);
-  if (threadIdx.x == 0) partials[blockIdx.x] = v[0];
+  write_wave_partial(partials, unit, ss);
 }
 
 template <typename T>
-__global__ __launch_bounds__(kElemThreads) void momentum_kernel(const MomTile* __restrict__ tiles,
-                                                                const MatGeom* __restrict__ geo,
-                                                                const MatPtrs* __restrict__ ptrs,
-                                                                double* __restrict__ partials,
-                                                                ElemParams prm) {
-  __shared__ float tile[kMomTile][kMomTile + 1];
-  __shared__ double red[1][4];
-  const MomTile t = tiles[blockIdx.x];
+__global__ __launch_bounds__(kElemThreads) void momentum_row_kernel(const MomTile* __restrict__ units,
+                                                                    const MatGeom* __restrict__ geo,
+                                                                    const MatPtrs* __restrict__ ptrs,
+                                                                    double* __restrict__ partials,
+                                                                    ElemParams prm) {
+  const int64_t unit = blockIdx.x;
+  const MomTile t = units[unit];
   const MatGeom& g = geo[t.mat];
   const MatPtrs p = ptrs[t.mat];
-  if (t.kind == 1) {
-    if (g.g_bf16)
-      momentum_row<T, uint16_t>(t, g, p, partials, prm, red);
-    else
-      momentum_row<T, float>(t, g, p, partials, prm, red);
-  } else if (g.g_bf16) {
-    momentum_tile<T, uint16_t>(t, g, p, partials, prm, tile, red);
-  } else {
-    momentum_tile<T, float>(t, g, p, partials, prm, tile, red);
-  }
+  if (g.g_bf16)
+    momentum_row<T, uint16_t>(t, unit, g, p, partials, prm);
+  else
+    momentum_row<T, float>(t, unit, g, p, partials, prm);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kElemThreads) void momentum_tile_kernel(const MomTile* __restrict__ units,
+                                                                     int64_t first,
+                                                                     const MatGeom* __restrict__ geo,
+                                                                     const MatPtrs* __restrict__ ptrs,
+                                                                     double* __restrict__ partials,
+                                                                     ElemParams prm) {
+  __shared__ T tile[kMomTileR][MomLds<T>::kPitch];
+  const int64_t unit = first + blockIdx.x;
+  const MomTile t = units[unit];
+  const MatGeom& g = geo[t.mat];
+  const MatPtrs p = ptrs[t.mat];
+  if (g.g_bf16)
+    momentum_tile<T, uint16_t>(t, unit, g, p, partials, prm, tile);
+  else
+    momentum_tile<T, float>(t, unit, g, p, partials, prm, tile);
 }
 
 // Sum of a matrix's block partials in block order, one wavefront per matrix:
@@ -224,14 +280,33 @@ __device__ __forceinline__ double ordered_sum(const double* p, int64_t n, int64_
   return wave_sum(s);
 }
 
-__global__ __launch_bounds__(64) void finalize_norm_kernel(const MatGeom* __restrict__ geo,
-                                                           const double* __restrict__ partials,
-                                                           MatScalars* __restrict__ scal, float eps) {
+// ||Y||^2 of one matrix from its units' partials, one 256-thread block per
+// matrix: thread t sums slots t, t + 256, ... in that order, eight loads in
+// flight at a time (the row units of a large matrix leave tens of thousands
+// of slots), then a fixed tree over the block.
+__global__ __launch_bounds__(kElemThreads) void finalize_norm_kernel(const MatGeom* __restrict__ geo,
+                                                                     const double* __restrict__ partials,
+                                                                     MatScalars* __restrict__ scal,
+                                                                     float eps) {
+  __shared__ double red[1][4];
   const int mat = blockIdx.x;
   const MatGeom& g = geo[mat];
-  const double ss = ordered_sum(partials + g.mom_tile0, g.mom_ntiles, 1);
+  const double* p = partials + kMomParts * g.mom_tile0;
+  const int64_t n = kMomParts * g.mom_ntiles;
+  double s = 0.0;
+  int64_t k = threadIdx.x;
+  for (; k + 7 * kElemThreads < n; k += 8 * kElemThreads) {
+    double v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[k + u * kElemThreads];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; k < n; k += kElemThreads) s += p[k];
+  double v[1] = {s};
+  block_sum<1>(v, red);
   if (threadIdx.x == 0) {
-    const double yn = sqrt(ss);
+    const double yn = sqrt(v[0]);
     scal[mat].y_norm = yn;
     scal[mat].s = (float)(1.0 / (yn + (double)eps));
   }
@@ -452,21 +527,34 @@ __global__ __launch_bounds__(kElemThreads) void adamw_kernel(const Chunk* __rest
 // ---------------------------------------------------------------------------
 // launchers
 
-hipError_t launch_momentum(int bf16, const MomTile* tiles, int64_t ntiles, const MatGeom* geo,
-                           const MatPtrs* ptrs, double* partials, ElemParams prm, hipStream_t st) {
-  if (ntiles <= 0) return hipSuccess;
-  if (bf16)
-    hipLaunchKernelGGL(momentum_kernel<uint16_t>, dim3((unsigned)ntiles), dim3(kElemThreads), 0, st,
-                       tiles, geo, ptrs, partials, prm);
-  else
-    hipLaunchKernelGGL(momentum_kernel<float>, dim3((unsigned)ntiles), dim3(kElemThreads), 0, st,
-                       tiles, geo, ptrs, partials, prm);
+hipError_t launch_momentum(int bf16, const MomTile* units, int64_t nrow, int64_t ntile,
+                           const MatGeom* geo, const MatPtrs* ptrs, double* partials,
+                           ElemParams prm, hipStream_t st) {
+  if (nrow > 0) {
+    if (bf16)
+      hipLaunchKernelGGL(momentum_row_kernel<uint16_t>, dim3((unsigned)nrow), dim3(kElemThreads), 0,
+                         st, units, geo, ptrs, partials, prm);
+    else
+      hipLaunchKernelGGL(momentum_row_kernel<float>, dim3((unsigned)nrow), dim3(kElemThreads), 0,
+                         st, units, geo, ptrs, partials, prm);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (ntile > 0) {
+    if (bf16)
+      hipLaunchKernelGGL(momentum_tile_kernel<uint16_t>, dim3((unsigned)ntile), dim3(kElemThreads),
+                         0, st, units, nrow, geo, ptrs, partials, prm);
+    else
+      hipLaunchKernelGGL(momentum_tile_kernel<float>, dim3((unsigned)ntile), dim3(kElemThreads),
+                         0, st, units, nrow, geo, ptrs, partials, prm);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_finalize_norm(int32_t nmat, const MatGeom* geo, const double* partials,
                                 MatScalars* scal, float eps, hipStream_t st) {
-  hipLaunchKernelGGL(finalize_norm_kernel, dim3(nmat), dim3(64), 0, st, geo, partials, scal, eps);
+  hipLaunchKernelGGL(finalize_norm_kernel, dim3(nmat), dim3(kElemThreads), 0, st, geo, partials,
+                     scal, eps);
   return hipGetLastError();
 }
 

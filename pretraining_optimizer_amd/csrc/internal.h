@@ -16,7 +16,8 @@ constexpr int kGemmTile = 256;      // output tile of the grouped GEMM (M and N)
 constexpr int kGemmThreads = 256;   // 4 wavefronts of 64, 2 x 2 over the tile
 constexpr int kPad = 256;           // Newton-Schulz dims are padded to this multiple
 constexpr int kRowSkewBytes = 128;  // extra bytes per row of every Newton-Schulz buffer
-constexpr int kMomTile = 64;        // momentum / pack tile (64 x 64 elements)
+constexpr int kMomTileR = 64;       // momentum / pack tile: 64 rows
+constexpr int kMomTileC = 128;      //   x 128 columns (512-byte rows of M)
 constexpr int kChunk = 16384;       // elements per chunk of the flat kernels
 constexpr int kElemThreads = 256;
 constexpr int kMaxXcd = 8;          // MI355X: 8 accelerator complex dies
@@ -53,7 +54,7 @@ struct GemmTile {
   int16_t tm, tn;
 };
 
-// One block of the momentum kernel.  kind 0: the 64 x 64 tile (tr, tc) of
+// One block of the momentum kernel.  kind 0: the 64 x 128 tile (tr, tc) of
 // the padded, original-orientation grid (the path that also writes a
 // transposed X_0); kind 1: columns [tc * 1024, tc * 1024 + 1024) of row tr
 // of that grid (matrices whose X_0 keeps M's orientation and has no
@@ -64,6 +65,7 @@ struct MomTile {
   int32_t kind;
 };
 constexpr int kMomRowSeg = 1024;   // columns per kind-1 block
+constexpr int kMomParts = 4;       // ||Y||^2 partial slots per unit (one per wavefront)
 
 struct Chunk {
   int32_t mat;
@@ -82,7 +84,7 @@ struct MatGeom {
   void* X[2];          // ping-pong iterate, [m_pad x n_pad]
   void* XT[2];         // its transpose, [n_pad x m_pad]
   void* U;             // compact update u, [rows x cols]
-  int64_t mom_tile0;   // first momentum tile (index into the partials array)
+  int64_t mom_tile0;   // first momentum unit; its partials start at kMomParts * mom_tile0
   int64_t mom_ntiles;
   int64_t chunk0;      // first flat chunk
   int64_t nchunks;
@@ -127,8 +129,11 @@ hipError_t launch_gemm(int bf16, int mode, const GemmProb* probs, const GemmTile
                        int symmetric, float ca, float cb, float cc, const MatPtrs* ptrs,
                        double* part, hipStream_t st);
 
-hipError_t launch_momentum(int bf16, const MomTile* tiles, int64_t ntiles, const MatGeom* geo,
-                           const MatPtrs* ptrs, double* partials, ElemParams prm, hipStream_t st);
+// units[0, nrow) are row segments (kind 1), units[nrow, nrow + ntile) tiles
+// (kind 0); one launch each.
+hipError_t launch_momentum(int bf16, const MomTile* units, int64_t nrow, int64_t ntile,
+                           const MatGeom* geo, const MatPtrs* ptrs, double* partials,
+                           ElemParams prm, hipStream_t st);
 
 hipError_t launch_finalize_norm(int32_t nmat, const MatGeom* geo, const double* partials,
                                 MatScalars* scal, float eps, hipStream_t st);

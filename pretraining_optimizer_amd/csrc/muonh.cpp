@@ -70,7 +70,8 @@ struct Plan {
   bool bf16 = true;
   size_t tsize = 2;
   std::vector<MatPlan> mats;
-  std::vector<MomTile> mom_tiles;
+  std::vector<MomTile> mom_tiles;   // row units (the first mom_rows), then tile units
+  int64_t mom_rows = 0;
   std::vector<Chunk> chunks;
   std::vector<GemmTile> tiles[3];
   int n_buckets = 0;
@@ -203,7 +204,8 @@ int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& op
   P.tsize = P.bf16 ? 2 : 4;
   P.mats.resize(n);
   std::map<std::pair<int64_t, int64_t>, int> buckets;
-  int64_t mom_tiles = 0, nchunks = 0;
+  int64_t nchunks = 0;
+  std::vector<MomTile> row_units, tile_units;
   for (int32_t i = 0; i < n; ++i) {
     MatPlan& m = P.mats[i];
     m.rows = mats[i].rows;
@@ -217,21 +219,23 @@ int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& op
     m.radius_in = mats[i].radius;
     buckets[{m.m_pad, m.n_pad}]++;
     const int64_t r_pad = m.tall ? m.n_pad : m.m_pad, c_pad = m.tall ? m.m_pad : m.n_pad;
-    m.mom_tile0 = mom_tiles;
+    // Momentum units: row segments where X_0 keeps M's orientation and has
+    // no transposed copy, 64 x 128 tiles otherwise.  All row units come first
+    // (one launch each kind); mom_tile0 is made global after the loop.
     if (P.bf16 && !m.tall) {
-      // X_0 keeps M's orientation and has no transposed copy: row segments.
       const int64_t nseg = (c_pad + kMomRowSeg - 1) / kMomRowSeg;
+      m.mom_tile0 = (int64_t)row_units.size();
       m.mom_ntiles = r_pad * nseg;
       for (int64_t r = 0; r < r_pad; ++r)
         for (int64_t sg = 0; sg < nseg; ++sg)
-          P.mom_tiles.push_back({i, (int32_t)r, (int32_t)sg, 1});
+          row_units.push_back({i, (int32_t)r, (int32_t)sg, 1});
     } else {
-      m.mom_ntiles = (r_pad / kMomTile) * (c_pad / kMomTile);
-      for (int64_t tr = 0; tr < r_pad / kMomTile; ++tr)
-        for (int64_t tc = 0; tc < c_pad / kMomTile; ++tc)
-          P.mom_tiles.push_back({i, (int32_t)tr, (int32_t)tc, 0});
+      m.mom_tile0 = -1 - (int64_t)tile_units.size();   // made global below
+      m.mom_ntiles = (r_pad / kMomTileR) * (c_pad / kMomTileC);
+      for (int64_t tr = 0; tr < r_pad / kMomTileR; ++tr)
+        for (int64_t tc = 0; tc < c_pad / kMomTileC; ++tc)
+          tile_units.push_back({i, (int32_t)tr, (int32_t)tc, 0});
     }
-    mom_tiles += m.mom_ntiles;
     const int64_t elems = m.rows * m.cols;
     m.chunk0 = nchunks;
     m.nchunks = (elems + kChunk - 1) / kChunk;
@@ -243,6 +247,11 @@ int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& op
     P.elem_bytes += (double)elems * ((m.g_bf16 ? 2.0 : 4.0) + 8.0 + 8.0);
   }
   P.n_buckets = (int)buckets.size();
+  P.mom_rows = (int64_t)row_units.size();
+  P.mom_tiles = std::move(row_units);
+  P.mom_tiles.insert(P.mom_tiles.end(), tile_units.begin(), tile_units.end());
+  for (auto& m : P.mats)
+    if (m.mom_tile0 < 0) m.mom_tile0 = P.mom_rows + (-1 - m.mom_tile0);
   // One partial slot per output tile and wavefront of the last B'X launch.
   for (auto& m : P.mats) {
     m.part0 = P.nparts;
@@ -290,7 +299,7 @@ int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& op
   for (int k = 0; k < 2; ++k) P.off_probs_gram[k] = take(sizeof(GemmProb) * n);
   P.off_probs_poly = take(sizeof(GemmProb) * n);
   for (int k = 0; k < 2; ++k) P.off_probs_apply[k] = take(sizeof(GemmProb) * n);
-  P.off_part_mom = take(sizeof(double) * P.mom_tiles.size());
+  P.off_part_mom = take(sizeof(double) * kMomParts * P.mom_tiles.size());
   P.off_part_radius = take(sizeof(double) * P.chunks.size());   // one ||W_0||^2 partial per chunk
   P.off_part_upd = take(sizeof(double) * 3 * (size_t)std::max<int64_t>(1, P.nparts));
   // Every Newton-Schulz buffer row is kRowSkewBytes longer than the padded
@@ -738,7 +747,8 @@ int enqueue_step(muonh_handle* h, hipStream_t st, const ElemParams& prm, const f
   } while (0)
 
   if ((rc = record(h, evi++, st))) return rc;
-  LAUNCH(launch_momentum(bf, h->at<MomTile>(pl.off_mom_tiles), (int64_t)pl.mom_tiles.size(), geo,
+  LAUNCH(launch_momentum(bf, h->at<MomTile>(pl.off_mom_tiles), pl.mom_rows,
+                         (int64_t)pl.mom_tiles.size() - pl.mom_rows, geo,
                          dptrs, h->at<double>(pl.off_part_mom), prm, st));
   LAUNCH(launch_finalize_norm(n, geo, h->at<double>(pl.off_part_mom), scal, pl.opt.ns_eps, st));
   if ((rc = record(h, evi++, st))) return rc;

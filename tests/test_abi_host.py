@@ -61,12 +61,12 @@ def test_plan_qwen3_17b_buckets_tiles_and_flops():
     dense = sum(oracle.muonh.ns_dense_flops(r, c) for r, c in wl.shapes)
     assert info.ns_dense_flops == pytest.approx(dense, rel=1e-12)
     assert info.ns_dense_flops == pytest.approx(6.795e13, rel=1e-3)
-    # momentum blocks: 64 x 64 tiles for tall matrices (their X_0 is packed
+    # momentum blocks: 64 x 128 tiles for tall matrices (their X_0 is packed
     # transposed), 1024-column row segments otherwise (bf16 plan)
-    assert info.mom_tiles == sum((r // 64) * (c // 64) if r > c else r * -(-c // 1024)
+    assert info.mom_tiles == sum((r // 64) * (c // 128) if r > c else r * -(-c // 1024)
                                  for r, c in wl.shapes)
     f32 = pm.plan_query(wl.shapes, pm.default_options(ns_dtype=pm.MUONH_F32))
-    assert f32.mom_tiles == sum(r * c for r, c in wl.shapes) // 4096
+    assert f32.mom_tiles == sum(r * c for r, c in wl.shapes) // 8192
     assert info.elem_bytes == pytest.approx(18.0 * wl.params())
 
 
