@@ -716,6 +716,143 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small-problem path.  When a plan's products have too few 256 x 256 tiles to
+// occupy the GPU (a handful of small matrices), one CU per big tile leaves
+// the rest idle and the step is a chain of single-CU launches.  This kernel
+// covers the same four products with 64 x 64 output tiles (4 wavefronts, one
+// 32 x 32 MFMA block each) and a plain load -> LDS -> MFMA loop over stages
+// of 64 bytes of K per operand row.  Only tiles and K stages inside the valid
+// (unpadded) dims are visited: the zero padding contributes nothing, and the
+// padding of every output stays as initialised (zero).  Every tile is
+// computed, so the Gram-type outputs are not mirrored.
+constexpr int kSmallTile = kSmallGemmTile;
+constexpr int kSmallRowBytes = 64;                  // K bytes per operand row per stage
+constexpr int kSmallPitch = kSmallRowBytes + 16;    // LDS row pitch
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
+    const GemmProb* __restrict__ probs, const GemmTile* __restrict__ tiles,
+    const MatScalars* __restrict__ scal, int first_iter, float ca, float cb, float cc,
+    const MatPtrs* __restrict__ ptrs, double* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint8_t lp[kSmallTile * kSmallPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t lq[kSmallTile * kSmallPitch];
+  // bf16 B'X reads X itself (K-major Q), as the big path does.
+  constexpr bool kQT = (MODE == kApply || MODE == kApplyLast) && sizeof(T) == 2;
+  constexpr int kKs = kSmallRowBytes / (int)sizeof(T);   // K elements per stage
+  static_assert(!kQT || kKs * kSmallTile * 2 == kGemmThreads * 16, "one K-major chunk per thread");
+
+  const GemmTile t = tiles[blockIdx.x];
+  const GemmProb pr = probs[t.prob];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int row0 = t.tm * kSmallTile, col0 = t.tn * kSmallTile;
+  const uint8_t* P = reinterpret_cast<const uint8_t*>(pr.P);
+  const uint8_t* Q = reinterpret_cast<const uint8_t*>(pr.Q);
+  // Row-major operands: thread = (row tid/4, 16-byte chunk tid%4).  K-major
+  // Q: thread = (k row tid/8, 8 columns from 8 (tid%8)), scattered into
+  // LDS as Q[n][k].
+  const int lr = tid >> 2, lc = tid & 3;
+  const int qr = tid >> 3, qc = tid & 7;
+  const int kend = min(pr.K, (pr.uk + kKs - 1) / kKs * kKs);
+  u32x4_t rp = {0u, 0u, 0u, 0u}, rq = {0u, 0u, 0u, 0u};
+  auto load = [&](int k0) {
+    rp = ld_global<u32x4_t>(P + ((size_t)(row0 + lr) * pr.ldp + k0) * sizeof(T) + lc * 16);
+    if constexpr (kQT)
+      rq = ld_global<u32x4_t>(Q + ((size_t)(k0 + qr) * pr.ldq + col0) * sizeof(T) + qc * 16);
+    else
+      rq = ld_global<u32x4_t>(Q + ((size_t)(col0 + lr) * pr.ldq + k0) * sizeof(T) + lc * 16);
+  };
+  auto stage = [&]() {
+    *reinterpret_cast<u32x4_t*>(lp + lr * kSmallPitch + lc * 16) = rp;
+    if constexpr (kQT) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint16_t*>(lq + (8 * qc + e) * kSmallPitch + qr * 2) =
+            (uint16_t)(rq[e >> 1] >> (16 * (e & 1)));
+    } else {
+      *reinterpret_cast<u32x4_t*>(lq + lr * kSmallPitch + lc * 16) = rq;
+    }
+  };
+  f32x16_t acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+  if (kend > 0) load(0);
+  for (int k0 = 0; k0 < kend; k0 += kKs) {
+    __syncthreads();   // the previous stage's fragments have been read
+    stage();
+    __syncthreads();
+    if (k0 + kKs < kend) load(k0 + kKs);
+    // Each run consumes 32 bytes of K per row: lanes 0-31 the first 16,
+    // lanes 32-63 the second (the fragment contract of Mfma<T>).
+#pragma unroll
+    for (int s2 = 0; s2 < kSmallRowBytes / 32; ++s2) {
+      const int off = s2 * 32 + (lane >> 5) * 16;
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(lp + (wr * 32 + (lane & 31)) * kSmallPitch + off);
+      const u32x4_t b = *reinterpret_cast<const u32x4_t*>(lq + (wc * 32 + (lane & 31)) * kSmallPitch + off);
+      Mfma<T>::run(acc, a, b);
+    }
+  }
+
+  // Epilogue, element for element as the big path's: register group g of
+  // the 32 x 32 block holds rows 8 g + 4 (lane / 32) + 0..3 of column lane % 32.
+  float alpha = 1.0f;
+  if (first_iter) {
+    const float sc = scal[pr.mat].s;
+    alpha = (MODE == kGram) ? sc * sc : sc;
+  }
+  T* O = reinterpret_cast<T*>(MODE == kApplyLast ? pr.U : pr.O);
+  T* OT = reinterpret_cast<T*>(pr.OT);
+  const T* E = reinterpret_cast<const T*>(pr.E);
+  const float* W = (MODE == kApplyLast) ? ptrs[pr.mat].w : nullptr;
+  float swu = 0.0f, suu = 0.0f, sww = 0.0f;
+  const int col = col0 + wc * 32 + (lane & 31);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int row = row0 + wr * 32 + g * 8 + (lane >> 5) * 4;
+    f32x4_t v;
+    v[0] = acc[4 * g + 0];
+    v[1] = acc[4 * g + 1];
+    v[2] = acc[4 * g + 2];
+    v[3] = acc[4 * g + 3];
+    if constexpr (MODE == kPoly) {
+      const f32x4_t e = Vec4<T>::load(E + (size_t)col * pr.lde + row);
+      v = cb * e + cc * v;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (row + q == col && col < pr.um) v[q] += ca;   // + a I
+    } else {
+      v *= alpha;
+    }
+    if constexpr (MODE == kApplyLast) {
+      if (col < pr.un && row < pr.um) {
+        const size_t base = pr.u_tall ? (size_t)col * pr.um + row : (size_t)row * pr.un + col;
+        const size_t step = pr.u_tall ? 1 : (size_t)pr.un;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (row + e < pr.um) {
+            Vec4<T>::store1(O + base + e * step, v[e]);
+            // the statistics use the stored (rounded) u, as the big path does
+            const float u = (sizeof(T) == 2) ? bf16_to_f32(f32_to_bf16(v[e])) : v[e];
+            const float w = W[base + e * step];
+            swu += w * u;
+            suu += u * u;
+            sww += w * w;
+          }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Vec4<T>::store1(O + (size_t)(row + e) * pr.ldo + col, v[e]);
+      if (MODE == kApply && OT) Vec4<T>::store(OT + (size_t)col * pr.ldot + row, v);
+    }
+  }
+  if constexpr (MODE == kApplyLast) {
+    // compact slots: one per valid tile (ceil(um/64) x ceil(un/64)) and wavefront
+    const int ntn = (pr.un + kSmallTile - 1) / kSmallTile;
+    write_stats(part, (int64_t)pr.part0 + ((int64_t)t.tm * ntn + t.tn) * 4 + wave, swu, suu, sww);
+  }
+}
+
 template <typename T>
 hipError_t launch_t(int mode, const GemmProb* probs, const GemmTile* tiles, int64_t ntiles,
                     const MatScalars* scal, int first_iter, int last_iter, int symmetric,
@@ -746,6 +883,33 @@ hipError_t launch_t(int mode, const GemmProb* probs, const GemmTile* tiles, int6
 
 }  // namespace
 
+template <typename T>
+hipError_t launch_small_t(int mode, const GemmProb* probs, const GemmTile* tiles, int64_t ntiles,
+                          const MatScalars* scal, int first_iter, int last_iter, float ca, float cb,
+                          float cc, const MatPtrs* ptrs, double* part, hipStream_t st) {
+  if (ntiles <= 0) return hipSuccess;
+  const dim3 grid((unsigned)ntiles), block(kGemmThreads);
+  switch (mode) {
+    case kGram:
+      hipLaunchKernelGGL((gemm_small_kernel<T, kGram>), grid, block, 0, st, probs, tiles, scal,
+                         first_iter, ca, cb, cc, ptrs, part);
+      break;
+    case kPoly:
+      hipLaunchKernelGGL((gemm_small_kernel<T, kPoly>), grid, block, 0, st, probs, tiles, scal,
+                         first_iter, ca, cb, cc, ptrs, part);
+      break;
+    default:
+      if (last_iter)
+        hipLaunchKernelGGL((gemm_small_kernel<T, kApplyLast>), grid, block, 0, st, probs, tiles,
+                           scal, first_iter, ca, cb, cc, ptrs, part);
+      else
+        hipLaunchKernelGGL((gemm_small_kernel<T, kApply>), grid, block, 0, st, probs, tiles, scal,
+                           first_iter, ca, cb, cc, ptrs, part);
+      break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(int bf16, int mode, const GemmProb* probs, const GemmTile* tiles,
                        int64_t ntiles, const MatScalars* scal, int first_iter, int last_iter,
                        int symmetric, float ca, float cb, float cc, const MatPtrs* ptrs,
@@ -755,6 +919,17 @@ hipError_t launch_gemm(int bf16, int mode, const GemmProb* probs, const GemmTile
                               ca, cb, cc, ptrs, part, st);
   return launch_t<float>(mode, probs, tiles, ntiles, scal, first_iter, last_iter, symmetric, ca,
                          cb, cc, ptrs, part, st);
+}
+
+hipError_t launch_gemm_small(int bf16, int mode, const GemmProb* probs, const GemmTile* tiles,
+                             int64_t ntiles, const MatScalars* scal, int first_iter, int last_iter,
+                             float ca, float cb, float cc, const MatPtrs* ptrs, double* part,
+                             hipStream_t st) {
+  if (bf16)
+    return launch_small_t<uint16_t>(mode, probs, tiles, ntiles, scal, first_iter, last_iter, ca, cb,
+                                    cc, ptrs, part, st);
+  return launch_small_t<float>(mode, probs, tiles, ntiles, scal, first_iter, last_iter, ca, cb, cc,
+                               ptrs, part, st);
 }
 
 }  // namespace muonh

@@ -21,6 +21,10 @@ constexpr int kMomTileC = 128;      //   x 128 columns (512-byte rows of M)
 constexpr int kChunk = 16384;       // elements per chunk of the flat kernels
 constexpr int kElemThreads = 256;
 constexpr int kMaxXcd = 8;          // MI355X: 8 accelerator complex dies
+constexpr int kSmallGemmTile = 64;  // output tile of the small-problem GEMM path
+// A plan takes the small-problem path when its largest product has fewer
+// 256 x 256 tiles than this (a quarter of the CUs).
+constexpr int kSmallPlanTiles = 64;
 
 enum GemmMode : int {
   kGram = 0,   // A = alpha * X X^T                       (alpha = s^2 on the first iteration)
@@ -42,6 +46,7 @@ struct GemmProb {
   int32_t M, N, K;
   int32_t ldp, ldq, lde, ldo, ldot;
   int32_t um, un;  // valid (unpadded) NS dims m x n of the matrix (kPoly: um for the diagonal)
+  int32_t uk;      // valid (unpadded) length of the contraction (n for X X^T, m otherwise)
   int32_t u_tall;  // 1: U is [un x um] (the matrix is tall), 0: U is [um x un]
   int32_t mat;     // matrix index
   int32_t part0;   // kApplyLast: first <W,u>/||u||^2/||W||^2 partial slot of the matrix
@@ -131,6 +136,14 @@ hipError_t launch_gemm(int bf16, int mode, const GemmProb* probs, const GemmTile
 
 // units[0, nrow) are row segments (kind 1), units[nrow, nrow + ntile) tiles
 // (kind 0); one launch each.
+// The small-problem path (64 x 64 tiles over the valid dims only, every tile
+// listed, no mirrored writes); same products and arguments.  Its last B'X
+// statistics use ceil(um/64) x ceil(un/64) x 4 slots per matrix.
+hipError_t launch_gemm_small(int bf16, int mode, const GemmProb* probs, const GemmTile* tiles,
+                             int64_t ntiles, const MatScalars* scal, int first_iter, int last_iter,
+                             float ca, float cb, float cc, const MatPtrs* ptrs, double* part,
+                             hipStream_t st);
+
 hipError_t launch_momentum(int bf16, const MomTile* units, int64_t nrow, int64_t ntile,
                            const MatGeom* geo, const MatPtrs* ptrs, double* partials,
                            ElemParams prm, hipStream_t st);

@@ -72,6 +72,7 @@ struct Plan {
   std::vector<MatPlan> mats;
   std::vector<MomTile> mom_tiles;   // row units (the first mom_rows), then tile units
   int64_t mom_rows = 0;
+  bool small_gemm = false;          // the small-problem GEMM path (64 x 64 tiles)
   std::vector<Chunk> chunks;
   std::vector<GemmTile> tiles[3];
   int n_buckets = 0;
@@ -252,32 +253,63 @@ int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& op
   P.mom_tiles.insert(P.mom_tiles.end(), tile_units.begin(), tile_units.end());
   for (auto& m : P.mats)
     if (m.mom_tile0 < 0) m.mom_tile0 = P.mom_rows + (-1 - m.mom_tile0);
-  // One partial slot per output tile and wavefront of the last B'X launch.
+  // GEMM path: 256 x 256 tiles, or, when the largest product (B'X) has too
+  // few of them to occupy the GPU, the small-problem path (64 x 64 tiles over
+  // the valid dims).  MUONH_GEMM_TILE=64 or 256 forces one of the two.
+  int64_t big_tiles = 0;
+  for (const auto& m : P.mats) big_tiles += (m.m_pad / kGemmTile) * (m.n_pad / kGemmTile);
+  P.small_gemm = big_tiles < kSmallPlanTiles;
+  if (const char* f = std::getenv("MUONH_GEMM_TILE")) {
+    if (std::strcmp(f, "64") == 0) P.small_gemm = true;
+    if (std::strcmp(f, "256") == 0) P.small_gemm = false;
+  }
+  auto cdiv = [](int64_t a, int64_t b) { return (a + b - 1) / b; };
+  // Partial slots of the last B'X launch: one per output tile and wavefront.
   for (auto& m : P.mats) {
     m.part0 = P.nparts;
-    m.nparts = (m.m_pad / kGemmTile) * (m.n_pad / kGemmTile) * (kGemmThreads / 64);
+    m.nparts = P.small_gemm
+                   ? cdiv(m.m, kSmallGemmTile) * cdiv(m.n, kSmallGemmTile) * (kGemmThreads / 64)
+                   : (m.m_pad / kGemmTile) * (m.n_pad / kGemmTile) * (kGemmThreads / 64);
     P.nparts += m.nparts;
   }
 
   // GEMM tile lists.
-  std::vector<std::tuple<int, int, int64_t>> d_gram, d_poly, d_apply;
-  for (const auto& m : P.mats) {
-    const int mt = (int)(m.m_pad / kGemmTile), nt = (int)(m.n_pad / kGemmTile);
-    d_gram.emplace_back(mt, mt, m.n_pad);
-    d_poly.emplace_back(mt, mt, m.m_pad);
-    d_apply.emplace_back(mt, nt, m.m_pad);
+  if (P.small_gemm) {
+    const int64_t kks = 64 / (int64_t)P.tsize;   // K elements per stage of the small kernel
+    for (int32_t p = 0; p < n; ++p) {
+      const auto& m = P.mats[p];
+      const int mt = (int)cdiv(m.m, kSmallGemmTile), nt = (int)cdiv(m.n, kSmallGemmTile);
+      for (int tm = 0; tm < mt; ++tm)
+        for (int tn = 0; tn < mt; ++tn) {
+          P.tiles[kGram].push_back({p, (int16_t)tm, (int16_t)tn});
+          P.tiles[kPoly].push_back({p, (int16_t)tm, (int16_t)tn});
+        }
+      for (int tm = 0; tm < mt; ++tm)
+        for (int tn = 0; tn < nt; ++tn) P.tiles[kApply].push_back({p, (int16_t)tm, (int16_t)tn});
+      const double t2 = 2.0 * kSmallGemmTile * kSmallGemmTile;
+      const double kn = (double)(cdiv(m.n, kks) * kks), km = (double)(cdiv(m.m, kks) * kks);
+      P.ns_exec += opt.ns_steps * t2 * ((double)mt * mt * kn + (double)mt * mt * km + (double)mt * nt * km);
+    }
+  } else {
+    std::vector<std::tuple<int, int, int64_t>> d_gram, d_poly, d_apply;
+    for (const auto& m : P.mats) {
+      const int mt = (int)(m.m_pad / kGemmTile), nt = (int)(m.n_pad / kGemmTile);
+      d_gram.emplace_back(mt, mt, m.n_pad);
+      d_poly.emplace_back(mt, mt, m.m_pad);
+      d_apply.emplace_back(mt, nt, m.m_pad);
+    }
+    const bool sym = opt.symmetric != 0;
+    P.tiles[kGram] = build_tile_list(d_gram, sym);
+    P.tiles[kPoly] = build_tile_list(d_poly, sym);
+    P.tiles[kApply] = build_tile_list(d_apply, false);
+    for (int k = 0; k < 3; ++k)
+      for (const auto& t : P.tiles[k])
+        if (t.prob >= 0) {
+          const auto& m = P.mats[t.prob];
+          const double K = (k == kGram) ? (double)m.n_pad : (double)m.m_pad;
+          P.ns_exec += opt.ns_steps * 2.0 * kGemmTile * kGemmTile * K;
+        }
   }
-  const bool sym = opt.symmetric != 0;
-  P.tiles[kGram] = build_tile_list(d_gram, sym);
-  P.tiles[kPoly] = build_tile_list(d_poly, sym);
-  P.tiles[kApply] = build_tile_list(d_apply, false);
-  for (int k = 0; k < 3; ++k)
-    for (const auto& t : P.tiles[k])
-      if (t.prob >= 0) {
-        const auto& m = P.mats[t.prob];
-        const double K = (k == kGram) ? (double)m.n_pad : (double)m.m_pad;
-        P.ns_exec += opt.ns_steps * 2.0 * kGemmTile * kGemmTile * K;
-      }
 
   // Workspace layout: tables first, then the large per-matrix buffers.
   size_t off = 0;
@@ -512,10 +544,12 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
     for (int k = 0; k < 3; ++k)
       for (const auto& t : pl.tiles[k]) gt[k] += t.prob >= 0;
     std::fprintf(stderr,
-                 "muonh: %d matrices in %d shape buckets, ns %s x%d; GEMM tiles gram %zu poly %zu "
-                 "apply %zu; %zu momentum tiles, %zu chunks; workspace %.3f GB; NS %.3e dense / "
-                 "%.3e executed FLOP per step\n",
-                 n, pl.n_buckets, pl.bf16 ? "bf16" : "fp32", pl.opt.ns_steps, gt[0], gt[1], gt[2],
+                 "muonh: %d matrices in %d shape buckets, ns %s x%d; GEMM tiles (%dx%d) gram %zu "
+                 "poly %zu apply %zu; %zu momentum tiles, %zu chunks; workspace %.3f GB; NS %.3e "
+                 "dense / %.3e executed FLOP per step\n",
+                 n, pl.n_buckets, pl.bf16 ? "bf16" : "fp32", pl.opt.ns_steps,
+                 pl.small_gemm ? kSmallGemmTile : kGemmTile, pl.small_gemm ? kSmallGemmTile : kGemmTile,
+                 gt[0], gt[1], gt[2],
                  pl.mom_tiles.size(), pl.chunks.size(), pl.total / 1e9, pl.ns_dense, pl.ns_exec);
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
@@ -586,6 +620,8 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
       a.K = N;
       a.ldp = a.ldq = LN;
       a.ldo = LM;
+      a.um = a.un = (int32_t)m.m;
+      a.uk = (int32_t)m.n;
       a.mat = i;
       GemmProb& c = apply[k][i];
       std::memset(&c, 0, sizeof(c));
@@ -605,6 +641,7 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
       c.ldot = LM;
       c.um = (int32_t)m.m;
       c.un = (int32_t)m.n;
+      c.uk = (int32_t)m.m;
       c.u_tall = m.tall;
       c.mat = i;
       c.part0 = (int32_t)m.part0;
@@ -615,7 +652,7 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
     b.O = h->ws + m.off_B;
     b.M = b.N = b.K = M;
     b.ldp = b.ldq = b.lde = b.ldo = LM;
-    b.um = (int32_t)m.m;
+    b.um = b.un = b.uk = (int32_t)m.m;
     b.mat = i;
   }
   auto up = [&](size_t off, const void* src, size_t bytes) -> int {
@@ -752,21 +789,26 @@ int enqueue_step(muonh_handle* h, hipStream_t st, const ElemParams& prm, const f
                          dptrs, h->at<double>(pl.off_part_mom), prm, st));
   LAUNCH(launch_finalize_norm(n, geo, h->at<double>(pl.off_part_mom), scal, pl.opt.ns_eps, st));
   if ((rc = record(h, evi++, st))) return rc;
+  // One grouped launch per product, on the plan's GEMM path.
+  auto gemm = [&](int mode, size_t probs_off, int first, int last) -> hipError_t {
+    const GemmProb* probs = h->at<GemmProb>(probs_off);
+    const int tk = mode == kGram ? kGram : (mode == kPoly ? kPoly : kApply);
+    const GemmTile* tiles = h->at<GemmTile>(pl.off_tiles[tk]);
+    const int64_t nt = (int64_t)pl.tiles[tk].size();
+    if (pl.small_gemm)
+      return launch_gemm_small(bf, mode, probs, tiles, nt, scal, first, last, pl.opt.ns_a,
+                               pl.opt.ns_b, pl.opt.ns_c, dptrs, part_upd, st);
+    return launch_gemm(bf, mode, probs, tiles, nt, scal, first, last, pl.opt.symmetric, pl.opt.ns_a,
+                       pl.opt.ns_b, pl.opt.ns_c, dptrs, part_upd, st);
+  };
   for (int it = 0; it < S; ++it) {
     const int par = it & 1;
     const int first = it == 0, last = it == S - 1;
-    LAUNCH(launch_gemm(bf, kGram, h->at<GemmProb>(pl.off_probs_gram[par]),
-                       h->at<GemmTile>(pl.off_tiles[kGram]), (int64_t)pl.tiles[kGram].size(), scal,
-                       first, 0, pl.opt.symmetric, pl.opt.ns_a, pl.opt.ns_b, pl.opt.ns_c, dptrs, part_upd, st));
+    LAUNCH(gemm(kGram, pl.off_probs_gram[par], first, 0));
     if ((rc = record(h, evi++, st))) return rc;
-    LAUNCH(launch_gemm(bf, kPoly, h->at<GemmProb>(pl.off_probs_poly),
-                       h->at<GemmTile>(pl.off_tiles[kPoly]), (int64_t)pl.tiles[kPoly].size(), scal,
-                       0, 0, pl.opt.symmetric, pl.opt.ns_a, pl.opt.ns_b, pl.opt.ns_c, dptrs, part_upd, st));
+    LAUNCH(gemm(kPoly, pl.off_probs_poly, 0, 0));
     if ((rc = record(h, evi++, st))) return rc;
-    LAUNCH(launch_gemm(bf, kApply, h->at<GemmProb>(pl.off_probs_apply[par]),
-                       h->at<GemmTile>(pl.off_tiles[kApply]), (int64_t)pl.tiles[kApply].size(),
-                       scal, first, last, pl.opt.symmetric, pl.opt.ns_a, pl.opt.ns_b, pl.opt.ns_c,
-                       dptrs, part_upd, st));
+    LAUNCH(gemm(kApply, pl.off_probs_apply[par], first, last));
     if ((rc = record(h, evi++, st))) return rc;
   }
   // <W,u>, ||u||^2 and ||W||^2 were reduced per tile by the last B'X launch.

@@ -10,6 +10,11 @@ hipError_t launch_gemm(int, int, const GemmProb*, const GemmTile*, int64_t, cons
                        int, int, int, float, float, float, const MatPtrs*, double*, hipStream_t) {
   return hipErrorNoDevice;
 }
+hipError_t launch_gemm_small(int, int, const GemmProb*, const GemmTile*, int64_t,
+                             const MatScalars*, int, int, float, float, float, const MatPtrs*,
+                             double*, hipStream_t) {
+  return hipErrorNoDevice;
+}
 hipError_t launch_momentum(int, const MomTile*, int64_t, int64_t, const MatGeom*, const MatPtrs*,
                            double*, ElemParams, hipStream_t) {
   return hipErrorNoDevice;

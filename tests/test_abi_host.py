@@ -70,12 +70,32 @@ def test_plan_qwen3_17b_buckets_tiles_and_flops():
     assert info.elem_bytes == pytest.approx(18.0 * wl.params())
 
 
-def test_plan_pads_ragged_shapes():
-    info = pm.plan_query([(1, 1), (300, 200), (129, 4096)], pm.default_options(symmetric=0))
+def test_plan_pads_ragged_shapes(monkeypatch):
+    shapes = [(1, 1), (300, 200), (129, 4096)]
+    monkeypatch.setenv("MUONH_GEMM_TILE", "256")
+    info = pm.plan_query(shapes, pm.default_options(symmetric=0))
     assert info.n_buckets == 3
     # (1,1) -> 256x256; (300,200) -> 256x512 (tall: m=200, n=300); (129,4096) -> 256x4096
     assert list(info.gemm_tiles) == [3, 3, 1 + 2 + 16]
+    # The same plan on the small-problem path: 64 x 64 tiles over the valid
+    # dims only, every tile listed: m = 1, 200, 129 -> 1, 4, 3 row tiles;
+    # n = 1, 300, 4096 -> 1, 5, 64 column tiles.
+    monkeypatch.setenv("MUONH_GEMM_TILE", "64")
+    small = pm.plan_query(shapes, pm.default_options(symmetric=0))
+    assert list(small.gemm_tiles) == [1 + 16 + 9, 1 + 16 + 9, 1 + 20 + 192]
+    # The path is chosen by the big-tile count of B'X when not forced: 19 < 64.
+    monkeypatch.delenv("MUONH_GEMM_TILE")
+    assert list(pm.plan_query(shapes, pm.default_options(symmetric=0)).gemm_tiles) == list(small.gemm_tiles)
     assert info.flat_chunks == 1 + 4 + 33
+
+
+def test_plan_gemm_path_threshold(monkeypatch):
+    monkeypatch.delenv("MUONH_GEMM_TILE", raising=False)
+    # 2048 x 2048 has 8 x 8 = 64 big B'X tiles: the big path; 63 of them in
+    # 63 matrices of 256 x 256: the small path (one 64-tile grid of 4 x 4 each).
+    assert list(pm.plan_query([(2048, 2048)]).gemm_tiles)[2] == 64
+    assert list(pm.plan_query([(256, 256)] * 63).gemm_tiles)[2] == 63 * 16
+    assert list(pm.plan_query([(256, 256)] * 64).gemm_tiles)[2] == 64
 
 
 def test_workspace_size_matches_plan():

@@ -35,9 +35,14 @@ def _gauss_fns(shapes, gdt, seed=0, gscale=1.0):
     return make_w, make_g
 
 
-def test_single_fp32_trajectory():
-    """256x128 fp32, 3 steps, eta 0.01, fp32 Newton-Schulz."""
-    announce("single fp32 256x128, 3 steps")
+@pytest.mark.parametrize("tile", ["auto", "256"])
+def test_single_fp32_trajectory(tile, monkeypatch):
+    """256x128 fp32, 3 steps, eta 0.01, fp32 Newton-Schulz; on the plan's own
+    GEMM path (the small-problem one: a single big tile) and forced onto the
+    256 x 256 path."""
+    if tile != "auto":
+        monkeypatch.setenv("MUONH_GEMM_TILE", tile)
+    announce(f"single fp32 256x128, 3 steps, GEMM tile {tile}")
     wl = inputs.workload("single")
     etas = [wl.eta(k) for k in range(wl.steps)]
     mw, mg = workload_fns(wl)
@@ -48,10 +53,13 @@ def test_single_fp32_trajectory():
 RAGGED = [(300, 200), (128, 640), (1, 37), (37, 1), (515, 515), (257, 1031), (1000, 260), (64, 64)]
 
 
+@pytest.mark.parametrize("tile", ["64", "256"])
 @pytest.mark.parametrize("ns,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
-def test_ragged_shapes(ns, tol):
-    """Shapes that span several 256-tiles, ragged tails, vectors, tall and wide."""
-    announce(f"ragged shapes, ns {ns}")
+def test_ragged_shapes(ns, tol, tile, monkeypatch):
+    """Shapes that span several tiles, ragged tails, vectors, tall and wide, on
+    both GEMM paths (64 x 64 tiles over the valid dims; 256 x 256 tiles)."""
+    monkeypatch.setenv("MUONH_GEMM_TILE", tile)
+    announce(f"ragged shapes, ns {ns}, GEMM tile {tile}")
     mw, mg = _gauss_fns(RAGGED, torch.bfloat16 if ns == "bf16" else torch.float32, seed=1)
     etas = [0.02, 0.015]
     reps = run_parity(RAGGED, mw, mg, etas, check=list(range(len(RAGGED))), ns=ns)
@@ -75,6 +83,24 @@ def test_stress_set_trajectory(ns, tol):
     etas = [wl.eta(k) for k in range(wl.steps)]
     reps = run_parity(wl.shapes, mw, mg, etas, check=check, ns=ns)
     check_reports(reps, tol, etas)
+
+
+@pytest.mark.parametrize("ns,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
+def test_stress_set_small_gemm_path(ns, tol, monkeypatch):
+    """The 64 stress matrices (dims 128-4096, ragged) forced onto the
+    small-problem GEMM path, one step; the oracle follows the same subset as
+    the trajectory test."""
+    monkeypatch.setenv("MUONH_GEMM_TILE", "64")
+    announce(f"stress set on the 64 x 64 GEMM path, ns {ns}, 1 step")
+    wl = inputs.workload("stress")
+    mw, mg = workload_fns(wl)
+    sizes = [r * c for r, c in wl.shapes]
+    order = np.argsort(sizes)
+    aspect = np.array([r / c for r, c in wl.shapes])
+    ar = np.argsort(aspect)
+    check = sorted(set(order[:8].tolist() + order[-2:].tolist() + ar[:2].tolist() + ar[-2:].tolist()))
+    reps = run_parity(wl.shapes, mw, mg, [wl.eta(0)], check=check, ns=ns)
+    check_reports(reps, tol, [wl.eta(0)])
 
 
 def test_diag170m_trajectory():
@@ -209,7 +235,8 @@ def test_bitwise_deterministic():
         assert torch.equal(a, b)
 
 
-def test_symmetric_and_full_tiles_agree():
+def test_symmetric_and_full_tiles_agree(monkeypatch):
+    monkeypatch.setenv("MUONH_GEMM_TILE", "256")   # the option belongs to the 256 x 256 path
     announce("symmetric vs full Gram tiles")
     shapes = [(512, 768), (1024, 300)]
     mw, mg = _gauss_fns(shapes, torch.bfloat16, seed=3)
