@@ -33,7 +33,11 @@
  *     after every kernel launch so a device fault is reported (MUONH_EHIP) by
  *     the step that caused it, naming the launch (slow; for debugging);
  *     MUONH_LOG=1 prints the plan (buckets, tile and chunk counts, workspace,
- *     FLOP per step) on stderr.
+ *     FLOP per step) on stderr; MUONH_GEMM_TILE=64 or 256 forces the GEMM
+ *     path (by default plans whose B'X product has fewer than 64 tiles of
+ *     256 x 256 use 64 x 64 tiles over the unpadded dims; results agree to
+ *     rounding, not bitwise).  Also read by muonh_workspace_size and
+ *     muonh_plan_query.
  */
 #ifndef MUONH_H_
 #define MUONH_H_
