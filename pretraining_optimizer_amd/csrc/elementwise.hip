@@ -197,15 +197,9 @@ __device__ __forceinline__ void momentum_row(const MomTile& t, int64_t unit, con
                                              const MatPtrs& p, double* partials,
                                              const ElemParams& prm) {
   static_assert(kMomRowSeg == kElemThreads * 4, "one 4-column group per thread");
-  // Every field is read before the first branch, so the scalar loads issue
-  // together (one round trip) rather than one behind each branch: with
-  // blocks this short the chain of dependent loads sets the pace.
   const int64_t rows = g.rows, cols = g.cols;
   const int64_t c_pad = g.c_pad, ldD = g.c_pad + g.ld_skew;
   T* D = reinterpret_cast<T*>(g.X[0]);
-  // (an empty use in scalar registers: the compiler would otherwise sink the
-  // loads of rows and cols behind the divergent branches below)
-  asm volatile("" ::"s"(rows), "s"(cols));
   const int64_t row = t.tr;
   const int64_t col = (int64_t)t.tc * kMomRowSeg + threadIdx.x * 4;
   const float beta = prm.beta;

@@ -218,8 +218,11 @@ def test_nonfinite_gradient_propagates_and_is_flagged():
     opt.close()
 
 
-def test_bitwise_deterministic():
-    announce("determinism")
+@pytest.mark.parametrize("tile", ["256", "64"])
+def test_bitwise_deterministic(tile, monkeypatch):
+    """Two runs give bitwise the same W and M, on either GEMM path."""
+    monkeypatch.setenv("MUONH_GEMM_TILE", tile)
+    announce(f"determinism, GEMM tile {tile}")
     wl = inputs.workload("diag170m")
     outs = []
     for _ in range(2):
