@@ -73,9 +73,10 @@ template <> struct GradLoad<float> {
 
 // ---------------------------------------------------------------------------
 // momentum + pack.  One 64 x 128 tile of the padded, original-orientation
-// grid per block (rows of 512 bytes of M: wider tiles stream faster, measured
-// on MI355X); thread (rr, cc) handles rows rr + 8q, columns cc..cc+3.  The
-// transposed X_0 is staged through LDS in the Newton-Schulz element type.
+// grid per 512-thread block (rows of 512 bytes of M: wider tiles stream
+// faster, measured on MI355X); thread (rr, cc) handles rows rr + 16q,
+// columns cc..cc+3.  The transposed X_0 is staged through LDS in the
+// Newton-Schulz element type.
 
 // ||Y||^2 partial of one momentum unit: one slot per wavefront (a fixed-order
 // fp64 shuffle tree inside the wavefront; no block-wide barrier).
@@ -107,7 +108,7 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, int64_t unit, co
                                               const ElemParams& prm,
                                               T (*tile)[MomLds<T>::kPitch]) {
   constexpr int kTpr = kMomTileC / 4;               // threads per row
-  constexpr int kRpp = kElemThreads / kTpr;         // rows per pass
+  constexpr int kRpp = kMomTileThreads / kTpr;      // rows per pass
   constexpr int kPasses = kMomTileR / kRpp;
   const int tid = threadIdx.x;
   const int cc = (tid % kTpr) * 4;
@@ -122,18 +123,14 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, int64_t unit, co
   const float beta = prm.beta;
   float ss = 0.0f;
 
-  // The tile is done as two halves of kHalf passes; all loads of a half are
-  // issued before its first store (M is written in place, so the compiler
-  // may not hoist them itself).  Two halves instead of one batch of all
-  // passes keep the register count, and so the occupancy, of a 64-row tile.
-  constexpr int kHalf = kPasses / 2;
-#pragma unroll 1
-  for (int h = 0; h < 2; ++h) {
-    f32x4_t gv[kHalf], mv[kHalf];
-    bool full[kHalf];
+  // All loads of the thread's rows are issued before its first store (M is
+  // written in place, so the compiler may not hoist them itself).
+  {
+    f32x4_t gv[kPasses], mv[kPasses];
+    bool full[kPasses];
 #pragma unroll
-    for (int q = 0; q < kHalf; ++q) {
-      const int64_t row = r0 + rr + kRpp * (h * kHalf + q);
+    for (int q = 0; q < kPasses; ++q) {
+      const int64_t row = r0 + rr + kRpp * q;
       const int64_t col = c0 + cc;
       full[q] = row < g.rows && vec_ok && col + 3 < g.cols;
       if (full[q]) {
@@ -143,8 +140,8 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, int64_t unit, co
       }
     }
 #pragma unroll
-    for (int q = 0; q < kHalf; ++q) {
-      const int tr_ = rr + kRpp * (h * kHalf + q);   // row inside the tile
+    for (int q = 0; q < kPasses; ++q) {
+      const int tr_ = rr + kRpp * q;   // row inside the tile
       const int64_t row = r0 + tr_;
       const int64_t col = c0 + cc;
       f32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -175,7 +172,7 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, int64_t unit, co
     __syncthreads();
     // output row oc (= tile column) holds the tile's 64 rows, 4 per thread
     constexpr int kTpo = kMomTileR / 4;             // threads per output row
-    constexpr int kOpp = kElemThreads / kTpo;       // output rows per pass
+    constexpr int kOpp = kMomTileThreads / kTpo;    // output rows per pass
     const int oe = (tid % kTpo) * 4, orow = tid / kTpo;
 #pragma unroll
     for (int q = 0; q < kMomTileC / kOpp; ++q) {
@@ -184,7 +181,13 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, int64_t unit, co
              tile[oe + 3][oc]);
     }
   }
-  write_wave_partial(partials, unit, ss);
+  // Eight wavefronts, kMomParts slots: slot w = wavefront w + wavefront w + 4.
+  static_assert(kMomTileThreads / 64 == 2 * kMomParts, "two wavefronts per slot");
+  __shared__ double red[kMomTileThreads / 64];
+  const double sw = wave_sum((double)ss);
+  if ((tid & 63) == 0) red[tid >> 6] = sw;
+  __syncthreads();
+  if (tid < kMomParts) partials[kMomParts * unit + tid] = red[tid] + red[tid + kMomParts];
 }
 
 // momentum + pack for a matrix whose X_0 keeps M's orientation and has no
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(kElemThreads) void momentum_row_kernel(const MomTil
 }
 
 template <typename T>
-__global__ __launch_bounds__(kElemThreads) void momentum_tile_kernel(const MomTile* __restrict__ units,
+__global__ __launch_bounds__(kMomTileThreads) void momentum_tile_kernel(const MomTile* __restrict__ units,
                                                                      int64_t first,
                                                                      const MatGeom* __restrict__ geo,
                                                                      const MatPtrs* __restrict__ ptrs,
@@ -536,10 +539,10 @@ hipError_t launch_momentum(int bf16, const MomTile* units, int64_t nrow, int64_t
   }
   if (ntile > 0) {
     if (bf16)
-      hipLaunchKernelGGL(momentum_tile_kernel<uint16_t>, dim3((unsigned)ntile), dim3(kElemThreads),
+      hipLaunchKernelGGL(momentum_tile_kernel<uint16_t>, dim3((unsigned)ntile), dim3(kMomTileThreads),
                          0, st, units, nrow, geo, ptrs, partials, prm);
     else
-      hipLaunchKernelGGL(momentum_tile_kernel<float>, dim3((unsigned)ntile), dim3(kElemThreads),
+      hipLaunchKernelGGL(momentum_tile_kernel<float>, dim3((unsigned)ntile), dim3(kMomTileThreads),
                          0, st, units, nrow, geo, ptrs, partials, prm);
   }
   return hipGetLastError();

@@ -18,6 +18,7 @@ constexpr int kPad = 256;           // Newton-Schulz dims are padded to this mul
 constexpr int kRowSkewBytes = 128;  // extra bytes per row of every Newton-Schulz buffer
 constexpr int kMomTileR = 64;       // momentum / pack tile: 64 rows
 constexpr int kMomTileC = 128;      //   x 128 columns (512-byte rows of M)
+constexpr int kMomTileThreads = 512;  // 8 wavefronts per tile: 4 rows of 4 columns per thread
 constexpr int kChunk = 16384;       // elements per chunk of the flat kernels
 constexpr int kElemThreads = 256;
 constexpr int kMaxXcd = 8;          // MI355X: 8 accelerator complex dies
