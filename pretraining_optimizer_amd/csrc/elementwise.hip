@@ -477,10 +477,18 @@ __device__ __forceinline__ void adamw4(f32x4_t& w, f32x4_t& m, f32x4_t& v, const
   }
 }
 
+// AdamW streams seven arrays (W, m, v read and written, g read): 128-thread
+// blocks over 512-element slices measured faster than the update kernel's
+// 256 x 1024 on MI355X.
+constexpr int kAdamwThreads = 128;
+constexpr int kAdamwSlice = kAdamwThreads * 4;
+constexpr int kAdamwSlicesPerChunk = kChunk / kAdamwSlice;
+static_assert(kChunk % kAdamwSlice == 0, "a chunk is a whole number of AdamW slices");
+
 template <typename G>
 __device__ __forceinline__ void adamw_slice(const Chunk& c, int s0, const AdamwPtrs& q,
                                             const AdamwParams& p) {
-  const int len = min(kSlice, c.len - s0);
+  const int len = min(kAdamwSlice, c.len - s0);
   float* W = q.w + c.start + s0;
   float* Mm = q.m + c.start + s0;
   float* V = q.v + c.start + s0;
@@ -506,11 +514,11 @@ __device__ __forceinline__ void adamw_slice(const Chunk& c, int s0, const AdamwP
   }
 }
 
-__global__ __launch_bounds__(kElemThreads) void adamw_kernel(const Chunk* __restrict__ chunks,
+__global__ __launch_bounds__(kAdamwThreads) void adamw_kernel(const Chunk* __restrict__ chunks,
                                                              const AdamwPtrs* __restrict__ ptrs,
                                                              AdamwParams prm) {
-  const Chunk c = chunks[blockIdx.x / kSlicesPerChunk];
-  const int s0 = (int)(blockIdx.x % kSlicesPerChunk) * kSlice;
+  const Chunk c = chunks[blockIdx.x / kAdamwSlicesPerChunk];
+  const int s0 = (int)(blockIdx.x % kAdamwSlicesPerChunk) * kAdamwSlice;
   if (s0 >= c.len) return;
   const AdamwPtrs q = ptrs[c.mat];
   if (q.g_bf16)
@@ -612,7 +620,7 @@ hipError_t launch_copy_update(int bf16, const void* U, int64_t count, float* dst
 hipError_t launch_adamw(const Chunk* chunks, int64_t nchunks, const AdamwPtrs* ptrs,
                         AdamwParams prm, hipStream_t st) {
   if (nchunks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)(nchunks * kSlicesPerChunk)), dim3(kElemThreads),
+  hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)(nchunks * kAdamwSlicesPerChunk)), dim3(kAdamwThreads),
                      0, st, chunks, ptrs, prm);
   return hipGetLastError();
 }
