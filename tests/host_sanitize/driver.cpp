@@ -170,6 +170,13 @@ int main() {
   }
   CHECK(muonh_destroy(nullptr) == MUONH_OK);
   CHECK(muonh_step(nullptr, one.data(), 1, nullptr, nullptr) == MUONH_EINVAL);
+  CHECK(muonh_step_graph(nullptr, one.data(), 1, nullptr, nullptr) == MUONH_EINVAL);
+  {
+    muonh_step_args a;
+    std::memset(&a, 0, sizeof(a));
+    a.elr = 0.01f;
+    CHECK(muonh_step_graph(nullptr, one.data(), 1, &a, nullptr) == MUONH_EINVAL);
+  }
   for (int s = -7; s <= 0; ++s) CHECK(muonh_status_str(s) != nullptr);
 
   // ---- learning-rate helpers (values are pinned against the oracle elsewhere)
