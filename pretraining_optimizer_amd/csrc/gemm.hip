@@ -178,7 +178,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
   // Sub-step s reads 16-byte chunk 2s (lanes 0-31) / 2s+1 (lanes 32-63).
   const int swz = swz128(lane & 15);
   const int a_off = (wr * 128 + (lane & 31)) * kRowBytes;
-  const int b_off = kOperandBytes + (wc * 128 + (lane & 31)) * kRowBytes;
+  // A diagonal tile of a Gram-type product (tm == tn) has P == Q: its B
+  // fragments are read from the staged P panel, and its Q loads go through a
+  // descriptor with no valid range (they return zeros without a memory
+  // access), which takes half of such a tile's operand traffic off the L2.
+  const bool diag = (MODE == kGram || MODE == kPoly) && t.tm == t.tn;
+  const int b_off = (diag ? 0 : kOperandBytes) + (wc * 128 + (lane & 31)) * kRowBytes;
   // K-major B fragments (kQT): lane l of 16-lane group g = l / 16 fetches the
   // 8 bytes at row 16 s + 4 h + 8 (g / 2) + (l % 16) / 4 of the stage and
   // column 32 j + 16 (g % 2) + 4 (l % 4) of the wavefront's 128 columns; the
@@ -254,8 +259,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
                              : reinterpret_cast<const uint8_t*>(pr.Q) + (size_t)col0 * qstride;
   const __amdgpu_buffer_rsrc_t prs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pbase), (short)0, -1, kBufferConfig);
-  const __amdgpu_buffer_rsrc_t qrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(qbase), (short)0, -1, kBufferConfig);
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(qbase), (short)0, __builtin_amdgcn_readfirstlane(diag ? 0 : -1),
+      kBufferConfig);
   const int pvoff = (int)(srow * pstride) + schunk * 16;
   const int qvoff = kQT ? (int)(qrow * qstride) + qchunk * 16 : (int)(srow * qstride) + schunk * 16;
   const int sst = srow * kRowBytes + ((schunk ^ swz128(srow & 15)) << 4);
