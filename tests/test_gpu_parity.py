@@ -249,10 +249,14 @@ def test_symmetric_and_full_tiles_agree(monkeypatch):
     check_reports(b, TOL_BF16, [0.02])
 
 
+@pytest.mark.parametrize("tile", ["auto", "256"])
 @pytest.mark.parametrize("mode", [pm.MUONH_MODE_MUON_WD, pm.MUONH_MODE_ELR_ALIGNED])
-def test_other_update_modes(mode):
-    """Ordinary Muon with decoupled weight decay (Eq. 3) and ELR-aligned Muon (Eq. 5)."""
-    announce(f"mode {mode}")
+def test_other_update_modes(mode, tile, monkeypatch):
+    """Ordinary Muon with decoupled weight decay (Eq. 3) and ELR-aligned Muon
+    (Eq. 5), on the plan's own GEMM path and on the 256 x 256 one."""
+    if tile != "auto":
+        monkeypatch.setenv("MUONH_GEMM_TILE", tile)
+    announce(f"mode {mode}, GEMM tile {tile}")
     shapes = [(256, 384), (640, 256)]
     mw, mg = _gauss_fns(shapes, torch.float32, seed=4)
     etas = [0.02, 0.01]
@@ -265,8 +269,11 @@ def test_other_update_modes(mode):
                 assert s["elr"] == pytest.approx(etas[rep.step], rel=1e-5)
 
 
-def test_nesterov_and_elr_scale_and_resume_radius():
-    announce("nesterov + per-matrix elr scale + given radii")
+@pytest.mark.parametrize("tile", ["auto", "256"])
+def test_nesterov_and_elr_scale_and_resume_radius(tile, monkeypatch):
+    if tile != "auto":
+        monkeypatch.setenv("MUONH_GEMM_TILE", tile)
+    announce(f"nesterov + per-matrix elr scale + given radii, GEMM tile {tile}")
     shapes = [(256, 256), (300, 512)]
     mw, mg = _gauss_fns(shapes, torch.float32, seed=5)
     reps = run_parity(shapes, mw, mg, [0.02, 0.02], check=[0, 1], ns="f32",
