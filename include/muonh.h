@@ -89,6 +89,10 @@ typedef struct muonh_options {
   int32_t mode;          /* MUONH_MODE_*, default MUONH_MODE_HYPERBALL              */
   float   weight_decay;  /* lambda of MUONH_MODE_MUON_WD, default 0                  */
   int32_t symmetric;     /* 1 (default): X X^T and A A computed on upper tiles only */
+  int32_t deterministic; /* 1 (default): every reduction runs in a fixed order (no
+                            floating-point atomics), so repeated steps on the same
+                            inputs are bitwise equal; 0 is accepted and behaves the
+                            same (there is no faster non-deterministic path)        */
   void*   workspace;     /* optional caller-owned device memory; NULL: library allocates */
   size_t  workspace_bytes;
 } muonh_options;

@@ -98,6 +98,8 @@ int check_options(const muonh_options& o) {
       !std::isfinite(o.weight_decay))
     return fail(MUONH_EINVAL, "non-finite or negative option value");
   if (o.nesterov != 0 && o.nesterov != 1) return fail(MUONH_EINVAL, "nesterov must be 0 or 1");
+  if (o.deterministic != 0 && o.deterministic != 1)
+    return fail(MUONH_EINVAL, "deterministic must be 0 or 1");
   return MUONH_OK;
 }
 
@@ -472,6 +474,7 @@ void muonh_default_options(muonh_options* opt) {
   opt->mode = MUONH_MODE_HYPERBALL;
   opt->weight_decay = 0.0f;
   opt->symmetric = 1;
+  opt->deterministic = 1;
   opt->workspace = nullptr;
   opt->workspace_bytes = 0;
 }

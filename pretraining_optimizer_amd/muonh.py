@@ -46,6 +46,7 @@ class muonh_options(ctypes.Structure):
                 ("ns_eps", ctypes.c_float), ("ns_dtype", ctypes.c_int32),
                 ("nesterov", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("weight_decay", ctypes.c_float), ("symmetric", ctypes.c_int32),
+                ("deterministic", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 

@@ -5,6 +5,7 @@
 // and argument checks; and init failing cleanly where no device is present.
 // Exits non-zero on the first failed check (a sanitizer report also fails).
 #include <cmath>
+#include <cstddef>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -171,6 +172,9 @@ int main() {
   CHECK(muonh_destroy(nullptr) == MUONH_OK);
   CHECK(muonh_step(nullptr, one.data(), 1, nullptr, nullptr) == MUONH_EINVAL);
   CHECK(muonh_step_graph(nullptr, one.data(), 1, nullptr, nullptr) == MUONH_EINVAL);
+  // The option struct's layout, as the Python binding mirrors it.
+  CHECK(sizeof(muonh_options) == 64 && offsetof(muonh_options, workspace) == 48);
+  CHECK(offsetof(muonh_options, deterministic) == 44);
   {
     muonh_step_args a;
     std::memset(&a, 0, sizeof(a));

@@ -41,6 +41,11 @@ def test_default_options():
     assert (o.ns_a, o.ns_b, o.ns_c) == pytest.approx(oracle.NS_COEFFS_QUINTIC)
     assert o.ns_eps == pytest.approx(1e-7)
     assert o.ns_dtype == pm.MUONH_BF16 and o.mode == pm.MUONH_MODE_HYPERBALL and o.symmetric == 1
+    assert o.deterministic == 1
+    # the flag sits in what was padding before the workspace pointer
+    assert mb.muonh_options.workspace.offset == 48 and ctypes.sizeof(mb.muonh_options) == 64
+    # 0 is accepted (the path is deterministic either way)
+    assert pm.plan_query([(8, 8)], pm.default_options(deterministic=0)).n_matrices == 1
 
 
 def _tiles(m_pad, n_pad, sym=True):
@@ -109,7 +114,7 @@ def test_workspace_size_matches_plan():
     dict(shapes=[(0, 5)]), dict(shapes=[(5, -1)]), dict(shapes=[(70000, 8)]),
     dict(opts=dict(ns_steps=0)), dict(opts=dict(ns_steps=17)), dict(opts=dict(ns_dtype=7)),
     dict(opts=dict(mode=9)), dict(opts=dict(nesterov=2)), dict(opts=dict(ns_eps=-1.0)),
-    dict(g_dtype=5),
+    dict(opts=dict(deterministic=2)), dict(g_dtype=5),
 ])
 def test_invalid_arguments_are_rejected(bad):
     shapes = bad.get("shapes", [(8, 8)])
