@@ -103,6 +103,19 @@ def test_stress_set_small_gemm_path(ns, tol, monkeypatch):
     check_reports(reps, tol, [wl.eta(0)])
 
 
+@pytest.mark.parametrize("ns,tol,tile", [("bf16", TOL_BF16, "256"), ("f32", TOL_F32, "256"),
+                                         ("bf16", TOL_BF16, "64")])
+def test_maximum_dimension(ns, tol, tile, monkeypatch):
+    """Matrices at the largest supported side, 65536 (tall and wide): a
+    contraction of 1024 K stages and 256 (1024 small) column tiles."""
+    monkeypatch.setenv("MUONH_GEMM_TILE", tile)
+    announce(f"maximum dimension 65536, ns {ns}, GEMM tile {tile}")
+    shapes = [(65536, 96), (100, 65536)]
+    mw, mg = _gauss_fns(shapes, torch.bfloat16 if ns == "bf16" else torch.float32, seed=21)
+    reps = run_parity(shapes, mw, mg, [0.02], check=[0, 1], ns=ns)
+    check_reports(reps, tol, [0.02])
+
+
 def test_diag170m_trajectory():
     """170M-class set (84 matrices, bf16 grads scaled by 1/sqrt(fan_in)), all 20
     steps of the linear ELR decay; the oracle follows layers 0 and 11."""
