@@ -116,6 +116,48 @@ def test_maximum_dimension(ns, tol, tile, monkeypatch):
     check_reports(reps, tol, [0.02])
 
 
+@pytest.mark.parametrize("tile", ["64", "256"])
+@pytest.mark.parametrize("ns", ["f32", "bf16"])
+def test_rank_one_gradient_gives_its_outer_product(ns, tile, monkeypatch):
+    """A rank-1 gradient G = x y^T has one singular value, so the
+    Newton-Schulz output is a multiple of x y^T and u_hat = x y^T / (|x||y|):
+    a closed form checked on the GPU path directly, not through the oracle.
+    x and y are small integers, so G is exactly rank 1 in fp32 and bf16.
+
+    Each B'X product keeps an iterate rank 1, but rounding it to the
+    operand type adds full-rank noise, and the remaining iterations multiply
+    small singular values by about 3.4 each (the iteration is built to grow
+    them).  In fp32 that leaves |u_hat - x y^T| below 1e-3.  In bf16 the
+    first rounding (2^-9) grows into spurious singular values of 0.08-0.12
+    next to the main one (0.7), on either GEMM path: the bf16 iteration
+    orthogonalises its own rounding error on an exactly rank-deficient input
+    (measured cosines 0.977 and 0.991 for these shapes).  What is checked
+    there is that the rank-1 direction dominates (cosine >= 0.95)."""
+    monkeypatch.setenv("MUONH_GEMM_TILE", tile)
+    announce(f"rank-1 gradient, ns {ns}, GEMM tile {tile}")
+    gen = torch.Generator().manual_seed(31)
+    for r, c in [(512, 384), (300, 1000)]:
+        x = torch.randint(-8, 9, (r, 1), generator=gen).double()
+        y = torch.randint(-8, 9, (c, 1), generator=gen).double()
+        x[0, 0], y[0, 0] = 5.0, -3.0   # never all zero
+        g = (x @ y.T).float()           # |entries| <= 64: exact in fp32 and bf16
+        w = torch.randn(r, c, generator=gen)
+        w = (w * (math.sqrt(r) / w.norm())).cuda()
+        m = torch.zeros_like(w)
+        gdt = torch.bfloat16 if ns == "bf16" else torch.float32
+        opt = pm.MuonH([w], [m], grad_dtype=gdt,
+                       ns_dtype=pm.MUONH_BF16 if ns == "bf16" else pm.MUONH_F32)
+        opt.step([g.to(gdt).cuda()], 0.01)
+        u = opt.copy_update(0).double().cpu()
+        torch.cuda.synchronize()
+        opt.close()
+        uh, v = u / u.norm(), (x @ y.T) / (x.norm() * y.norm())
+        if ns == "f32":
+            assert (uh - v).norm().item() <= 1e-3, (r, c)
+        else:
+            assert (uh * v).sum().item() >= 0.95, (r, c)
+
+
 def test_diag170m_trajectory():
     """170M-class set (84 matrices, bf16 grads scaled by 1/sqrt(fan_in)), all 20
     steps of the linear ELR decay; the oracle follows layers 0 and 11."""
