@@ -59,11 +59,16 @@ def _trajectory(ns, graph, mode=pm.MUONH_MODE_HYPERBALL):
     return snaps
 
 
+@pytest.mark.parametrize("tile", ["auto", "256"])
 @pytest.mark.parametrize("ns", ["bf16", "f32"])
 @pytest.mark.parametrize("mode", [pm.MUONH_MODE_HYPERBALL, pm.MUONH_MODE_MUON_WD,
                                   pm.MUONH_MODE_ELR_ALIGNED])
-def test_graph_replays_match_ordinary_steps(ns, mode):
-    announce(f"graph replays vs ordinary steps, ns {ns}, mode {mode}")
+def test_graph_replays_match_ordinary_steps(ns, mode, tile, monkeypatch):
+    """On the plan's own GEMM path (small-problem, for these shapes) and on
+    the 256 x 256 one."""
+    if tile != "auto":
+        monkeypatch.setenv("MUONH_GEMM_TILE", tile)
+    announce(f"graph replays vs ordinary steps, ns {ns}, mode {mode}, GEMM tile {tile}")
     a = _trajectory(ns, graph=False, mode=mode)
     b = _trajectory(ns, graph=True, mode=mode)
     for k, ((wa, ma, sa), (wb, mb, sb)) in enumerate(zip(a, b)):
