@@ -174,7 +174,10 @@ int muonh_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
 int muonh_step_graph(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
                      const muonh_step_args* args, void* stream);
 
-/* Synchronise the handle's last stream, then copy the n radii to host. */
+/* Synchronise the handle's last stream, then copy the n radii to host.  A
+ * radius measured at init is rounded to float when measured, so these are
+ * exactly the R the steps use: a new handle given them as the descriptors'
+ * radius, with the saved W and M, continues bit for bit.                  */
 int muonh_get_radii(muonh_handle* h, float* out, int32_t n);
 
 /* Synchronise, then copy the n per-matrix statistics of the last step. */

@@ -443,7 +443,10 @@ __global__ __launch_bounds__(64) void finalize_radius_kernel(const MatGeom* __re
   const int mat = blockIdx.x;
   const MatGeom& g = geo[mat];
   const double ss = ordered_sum(partials + g.chunk0, g.nchunks, 1);
-  if (threadIdx.x == 0 && need[mat]) scal[mat].R = sqrt(ss);
+  // R is carried as a float across the interface (descriptor and muonh_get_radii), so the
+  // measured value is rounded to float here: the steps then use exactly the R a caller
+  // reads back and passes to a new handle, and a resume continues bit for bit.
+  if (threadIdx.x == 0 && need[mat]) scal[mat].R = (double)(float)sqrt(ss);
 }
 
 template <typename T>

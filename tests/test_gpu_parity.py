@@ -337,6 +337,43 @@ def test_nesterov_and_elr_scale_and_resume_radius(tile, monkeypatch):
     check_reports(reps, TOL_F32, [0.02, 0.02])
 
 
+@pytest.mark.parametrize("tile", ["auto", "256"])
+def test_resume_from_saved_state_is_bitwise(tile, monkeypatch):
+    """All state is the caller's (W, M) plus the radii: 3 steps, a new handle
+    built from the saved W, M and R (muonh_get_radii passed back as the
+    descriptors' radius), 2 more steps -- bitwise the same as 5 steps on one
+    handle."""
+    if tile != "auto":
+        monkeypatch.setenv("MUONH_GEMM_TILE", tile)
+    announce(f"resume from saved state, GEMM tile {tile}")
+    shapes = [(300, 200), (128, 640), (515, 515)]
+    mw, mg = _gauss_fns(shapes, torch.bfloat16, seed=41)
+    etas = [0.02, 0.015, 0.012, 0.01, 0.008]
+
+    def run(split):
+        ws = [mw(i).cuda() for i in range(len(shapes))]
+        ms = [torch.zeros_like(w) for w in ws]
+        opt = pm.MuonH(ws, ms, grad_dtype=torch.bfloat16)
+        for k, eta in enumerate(etas):
+            if k == split:
+                radii = opt.radii()
+                saved_w = [w.clone() for w in ws]
+                saved_m = [m.clone() for m in ms]
+                opt.close()
+                del ws, ms
+                torch.cuda.synchronize()
+                ws, ms = saved_w, saved_m
+                opt = pm.MuonH(ws, ms, grad_dtype=torch.bfloat16, radii=radii)
+            opt.step([mg(k, i).cuda() for i in range(len(shapes))], eta, step=k)
+        torch.cuda.synchronize()
+        out = [w.clone() for w in ws] + [m.clone() for m in ms]
+        opt.close()
+        return out
+
+    for a, b in zip(run(split=None), run(split=3)):
+        assert torch.equal(a, b)
+
+
 def test_step_list_mismatch_is_rejected():
     announce("mismatch errors")
     dev = torch.device("cuda")
