@@ -324,6 +324,45 @@ def test_other_update_modes(mode, tile, monkeypatch):
                 assert s["elr"] == pytest.approx(etas[rep.step], rel=1e-5)
 
 
+@pytest.mark.parametrize("mode", [pm.MUONH_MODE_MUON_WD, pm.MUONH_MODE_ELR_ALIGNED])
+def test_other_modes_zero_gradient_beside_a_live_one(mode):
+    """A zero gradient in the Eq. (3) and Eq. (5) modes, in the same step as a
+    matrix with a live gradient: u = 0 leaves only the decay (Eq. 3) or W
+    unchanged with eta_t = 0 (Eq. 5), the other matrix follows the oracle, and
+    nothing is flagged non-finite."""
+    announce(f"zero gradient beside a live one, mode {mode}")
+    eta, lam = 0.02, 0.1
+    shapes = [(96, 160), (192, 128)]
+    mw, mg = _gauss_fns(shapes, torch.float32, seed=9)
+    w0 = [mw(i) for i in range(2)]
+    g = [torch.zeros(shapes[0]), mg(0, 1)]
+    ws = [w.cuda() for w in w0]
+    ms = [torch.zeros_like(w) for w in ws]
+    opt = pm.MuonH(ws, ms, grad_dtype=torch.float32, ns_dtype=pm.MUONH_F32, mode=mode,
+                   weight_decay=lam)
+    opt.step([x.cuda() for x in g], eta)
+    st = opt.stats()
+    u1 = opt.copy_update(1).cpu().double().numpy()
+    torch.cuda.synchronize()
+    opt.close()
+    assert all(x["nonfinite"] == 0 for x in st)
+    assert st[0]["u_norm"] == 0.0 and st[0]["elr"] == 0.0
+    y1 = oracle.ns_input(oracle.momentum_update(np.zeros(shapes[1]), g[1].numpy(), 0.95),
+                         g[1].numpy(), 0.95, False)
+    u1_ref = oracle.newton_schulz(y1)
+    assert rel(unit(u1), unit(u1_ref)) <= TOL_F32
+    if mode == pm.MUONH_MODE_MUON_WD:
+        ref = [oracle.muon_wd_update(w0[0].numpy(), np.zeros(shapes[0]), eta, lam),
+               oracle.muon_wd_update(w0[1].numpy(), u1_ref, eta, lam)]
+    else:
+        ref = [oracle.elr_aligned_update(w0[0].numpy(), np.zeros(shapes[0]), eta)[0],
+               oracle.elr_aligned_update(w0[1].numpy(), u1_ref, eta)[0]]
+        assert torch.equal(ws[0].cpu(), w0[0])
+        assert st[1]["elr"] == pytest.approx(eta, rel=1e-5)
+    for w, r in zip(ws, ref):
+        assert rel(w.cpu().double().numpy(), r) <= 1e-5
+
+
 @pytest.mark.parametrize("tile", ["auto", "256"])
 def test_nesterov_and_elr_scale_and_resume_radius(tile, monkeypatch):
     if tile != "auto":
