@@ -227,7 +227,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+        print(f"bench.py: the benchmark runs the step on one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); the step is not sharded across GPUs.", file=sys.stderr)
         sys.exit(2)
 
