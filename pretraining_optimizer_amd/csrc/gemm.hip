@@ -571,7 +571,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
       // <W,u>, ||u||^2 and ||W||^2 over the stored (bf16) u and the matching
       // W elements (U and W share the layout).  W is read in batches of 8
       // rows of 8 per lane, double-buffered, the first batch issued before
-      // the sub-tile goes through LDS.
+      // the sub-tile goes through LDS; chunks that cannot take 16-byte loads
+      // are read element by element in the same batches.
       int rbase, cbase, nrow, ncol, ld;
       if (!pr.u_tall) {
         rbase = wrow0; cbase = wcol0; nrow = pr.um; ncol = pr.un; ld = pr.un;
@@ -597,8 +598,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
             wb[buf][k][0] = ld_global<f32x4_t>(wptr(it0 + k));
             wb[buf][k][1] = ld_global<f32x4_t>(wptr(it0 + k) + 4);
           } else {
-            wb[buf][k][0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            wb[buf][k][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // Ragged edge, or a leading dimension that is not a multiple of 8:
+            // element loads, issued here with the rest of the batch rather than
+            // one round trip per chunk in the reduction below.
+            const int gr = rbase + (it0 + k) * 4 + (lane >> 4), gc = cbase + (lane & 15) * 8;
+            const float* wp = wptr(it0 + k);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              float v = 0.0f;
+              if (gr < nrow && gc + q < ncol) v = wp[q];
+              wb[buf][k][q >> 2][q & 3] = v;
+            }
           }
         }
       };
@@ -632,13 +642,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
               sww += w * w;
             }
           } else {
-            const float* wp = wptr(it);
 #pragma unroll
             for (int q = 0; q < 8; ++q)
               if (gc + q < ncol) {
                 const uint16_t h = (uint16_t)(x[k][q >> 1] >> (16 * (q & 1)));
                 st_global<uint16_t>(d + q, h);
-                const float u = __uint_as_float((uint32_t)h << 16), w = wp[q];
+                const float u = __uint_as_float((uint32_t)h << 16), w = wb[cur][k][q >> 2][q & 3];
                 swu += w * u;
                 suu += u * u;
                 sww += w * w;
