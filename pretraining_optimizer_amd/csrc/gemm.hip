@@ -680,6 +680,23 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int col = col0 + wc * 128 + j * 32 + (lane & 31);
+        // The block's W elements, loaded before any store to U so that the
+        // loads are in flight together (the compiler cannot move a load of W
+        // past a store to U on its own).
+        float wv[4][4];
+        if constexpr (MODE == kApplyLast) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int row = row0 + wr * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
+            const size_t base = pr.u_tall ? (size_t)col * pr.um + row : (size_t)row * pr.un + col;
+            const size_t step = pr.u_tall ? 1 : (size_t)pr.un;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              wv[g][e] = 0.0f;
+              if (col < pr.un && row + e < pr.um) wv[g][e] = W[base + e * step];
+            }
+          }
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int row = row0 + wr * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
@@ -707,7 +724,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(
               for (int e = 0; e < 4; ++e)
                 if (row + e < pr.um) {
                   Vec4<T>::store1(O + base + e * step, v[e]);   // + <W,u>, ||u||^2, ||W||^2 over it
-                  const float w = W[base + e * step];
+                  const float w = wv[g][e];
                   swu += w * v[e];
                   suu += v[e] * v[e];
                   sww += w * w;
@@ -822,6 +839,21 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
   const float* W = (MODE == kApplyLast) ? ptrs[pr.mat].w : nullptr;
   float swu = 0.0f, suu = 0.0f, sww = 0.0f;
   const int col = col0 + wc * 32 + (lane & 31);
+  // W elements of the lane, loaded before any store to U (in flight together).
+  float wv[4][4];
+  if constexpr (MODE == kApplyLast) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int row = row0 + wr * 32 + g * 8 + (lane >> 5) * 4;
+      const size_t base = pr.u_tall ? (size_t)col * pr.um + row : (size_t)row * pr.un + col;
+      const size_t step = pr.u_tall ? 1 : (size_t)pr.un;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        wv[g][e] = 0.0f;
+        if (col < pr.un && row + e < pr.um) wv[g][e] = W[base + e * step];
+      }
+    }
+  }
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int row = row0 + wr * 32 + g * 8 + (lane >> 5) * 4;
@@ -849,7 +881,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_small_kernel(
             Vec4<T>::store1(O + base + e * step, v[e]);
             // the statistics use the stored (rounded) u, as the big path does
             const float u = (sizeof(T) == 2) ? bf16_to_f32(f32_to_bf16(v[e])) : v[e];
-            const float w = W[base + e * step];
+            const float w = wv[g][e];
             swu += w * u;
             suu += u * u;
             sww += w * w;
