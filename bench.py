@@ -67,6 +67,56 @@ def per_kernel_work(shapes, ns_steps, tsize, gsize):
     return f, b, params
 
 
+def floor_flops(shapes, ns_steps):
+    """The method's own Newton-Schulz work per step: the Gram products X X^T
+    and A A are symmetric, so half of each suffices (m^2 n and m^3 per
+    iteration), and B X is a full product (2 m^2 n): 3 m^2 n + m^3."""
+    out = 0.0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        out += ns_steps * (3.0 * m * m * n + 1.0 * m * m * m)
+    return out
+
+
+def exec_flops(shapes, ns_steps, tsize, small: bool, symmetric: bool = True):
+    """MFMA FLOP the grouped GEMM issues per step, per product, as the
+    library plans it: on the 256 x 256 path every listed output tile runs the
+    padded contraction (upper tiles only for X X^T and A A when symmetric);
+    on the 64 x 64 path every valid tile runs the valid contraction rounded
+    up to its 64-byte K stage."""
+    def cdiv(a, b):
+        return (a + b - 1) // b
+    out = {"ns_gram": 0.0, "ns_poly": 0.0, "ns_apply": 0.0}
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        if small:
+            kks = 64 // tsize
+            mt, nt = cdiv(m, 64), cdiv(n, 64)
+            t2 = 2.0 * 64 * 64
+            out["ns_gram"] += ns_steps * t2 * mt * mt * cdiv(n, kks) * kks
+            out["ns_poly"] += ns_steps * t2 * mt * mt * cdiv(m, kks) * kks
+            out["ns_apply"] += ns_steps * t2 * mt * nt * cdiv(m, kks) * kks
+        else:
+            mp, np_ = cdiv(m, 256) * 256, cdiv(n, 256) * 256
+            mt, nt = mp // 256, np_ // 256
+            tri = mt * (mt + 1) // 2 if symmetric else mt * mt
+            t2 = 2.0 * 256 * 256
+            out["ns_gram"] += ns_steps * t2 * tri * np_
+            out["ns_poly"] += ns_steps * t2 * tri * mp
+            out["ns_apply"] += ns_steps * t2 * mt * nt * mp
+    return out
+
+
+def plan_exec_flops(shapes, ns_steps, tsize, plan_total):
+    """exec_flops on the GEMM path the library's plan took (the one whose
+    total equals the plan's executed FLOP)."""
+    for small in (False, True):
+        ex = exec_flops(shapes, ns_steps, tsize, small)
+        if abs(sum(ex.values()) - plan_total) <= 1e-9 * max(plan_total, 1.0):
+            return ex
+    raise RuntimeError("the executed-FLOP model matches neither GEMM path of the plan")
+
+
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_apply_qwen3_1.7b_traffic.md")
 KERNEL_SOURCES = ("gemm.hip", "device_util.h", "internal.h")
 
@@ -117,26 +167,35 @@ def blas_threads() -> int:
     return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
 
 
-def cpu_baseline(wl, ws_dev, grads_dev, eta, layer_mats: int):
-    """The CPU oracle (fp64 NumPy, as it stands) on one step of the first
-    `layer_mats` matrices, scaled to the whole set by FLOP share."""
-    import numpy as np
+def cpu_baseline(wl, ws_cpu, grads_cpu, eta, indices):
+    """The CPU oracle (fp64 NumPy, as it stands) timed on one step of the
+    matrices in `indices` (every matrix of the workload by default), one
+    matrix at a time so the host holds one matrix's fp64 state at once.
+    Only the oracle step itself is inside the timed region; with a subset
+    the time is scaled to the whole set by Newton-Schulz FLOP share."""
     import inputs
     import oracle
-    idx = list(range(layer_mats))
-    states = [oracle.OracleMatrixState.from_arrays(inputs.to_numpy64(ws_dev[i])) for i in idx]
-    gs = [inputs.to_numpy64(grads_dev[i]) for i in idx]
-    t0 = time.perf_counter()
-    oracle.muonh_step(states, gs, eta)
-    dt = time.perf_counter() - t0
     from oracle.muonh import ns_dense_flops
-    share = sum(ns_dense_flops(*wl.shapes[i]) for i in idx) / sum(ns_dense_flops(*s) for s in wl.shapes)
+    dt = 0.0
+    for j, i in enumerate(indices):
+        st = [oracle.OracleMatrixState.from_arrays(inputs.to_numpy64(ws_cpu[j]))]
+        g = [inputs.to_numpy64(grads_cpu[j])]
+        t0 = time.perf_counter()
+        oracle.muonh_step(st, g, eta)
+        dt += time.perf_counter() - t0
+        del st, g
+    share = sum(ns_dense_flops(*wl.shapes[i]) for i in indices) / sum(ns_dense_flops(*s) for s in wl.shapes)
     full = dt / share
+    if len(indices) == len(wl.shapes):
+        sample = (f"full step: one oracle step (fp64 NumPy) over all {len(indices)} matrices "
+                  f"took {dt:.2f} s")
+    else:
+        sample = (f"one oracle step (fp64 NumPy) over {len(indices)} of {len(wl.shapes)} matrices "
+                  f"({share:.4f} of the step's Newton-Schulz FLOP) took {dt:.2f} s; "
+                  f"scaled by FLOP share to {full:.1f} s per full step")
     return {"value": 1.0 / full, "unit": "steps/s", "cores": blas_threads(), "kind": "oracle",
-            "sample": f"one oracle step (fp64 NumPy) over matrices 0-{layer_mats - 1} "
-                      f"({share:.4f} of the step's Newton-Schulz FLOP) took {dt:.2f} s; "
-                      f"scaled by FLOP share to {full:.1f} s per full step",
-            "seconds_sample": dt, "host_cpus": os.cpu_count()}
+            "sample": sample, "seconds_sample": dt, "seconds_full_step": full,
+            "host_cpus": os.cpu_count(), "blas_threads": blas_threads()}
 
 
 def hbm_ceiling(n_elems: int, dev) -> dict:
@@ -211,8 +270,9 @@ def main():
     ap.add_argument("--workload", default="qwen3_1.7b")
     ap.add_argument("--ns-dtype", choices=("bf16", "f32"), default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-mats", type=int, default=7,
-                    help="matrices the CPU oracle times (default: one layer)")
+    ap.add_argument("--cpu-mats", type=int, default=0,
+                    help="time the CPU oracle on the first N matrices only and scale by FLOP "
+                         "share (default 0: a full step over every matrix)")
     ap.add_argument("--grad-sets", type=int, default=4)
     ap.add_argument("--no-adamw", action="store_true",
                     help="skip timing the AdamW step of the non-MuonH parameters")
@@ -251,8 +311,11 @@ def main():
     torch.cuda.synchronize()
     cpu_inputs = None
     if not args.no_cpu_baseline:
-        # keep the step-0 inputs of the sampled matrices for the oracle
-        cpu_inputs = ([w.clone() for w in ws[:args.cpu_mats]], pool[0][:args.cpu_mats])
+        # host copies of the step-0 inputs of the timed matrices for the oracle
+        # (W_0 before any step; gradients of step 0)
+        n_cpu = len(wl.shapes) if args.cpu_mats <= 0 else min(args.cpu_mats, len(wl.shapes))
+        cpu_idx = list(range(n_cpu))
+        cpu_inputs = ([ws[i].cpu() for i in cpu_idx], [pool[0][i].cpu() for i in cpu_idx])
 
     if args.copy_calibration > 0:
         n = args.copy_calibration // 4
@@ -313,40 +376,60 @@ def main():
     flops, bytes_, params = per_kernel_work(wl.shapes, S, tsize, gsize)
     per_step = {k: v / nt for k, v in phases.items()}
     peak = PEAK_BF16_TFLOPS if ns == "bf16" else PEAK_F32_TFLOPS
-    # launches per step of each NS kernel and its share of the dense FLOP
+    # Per NS kernel: launches per step and FLOP per step three ways --
+    #   alg:   the method's own work (X X^T and A A symmetric: m^2 n and m^3
+    #          per iteration; B X a full product, 2 m^2 n), the roofline's count;
+    #   exec:  the MFMA FLOP the grouped GEMM issues (padding, upper tiles);
+    #   dense: the dense-equivalent count (2 m^2 n, 2 m^3, 2 m^2 n).
     launches = {"ns_gram": S, "ns_poly": S, "ns_apply": S - 1, "ns_apply_last": 1}
-    fl = {"ns_gram": flops["ns_gram"], "ns_poly": flops["ns_poly"],
-          "ns_apply": flops["ns_apply"] * (S - 1) / S, "ns_apply_last": flops["ns_apply"] / S}
+    ex = plan_exec_flops(wl.shapes, S, tsize, info.ns_exec_flops)
+    last = {"ns_gram": 1.0, "ns_poly": 1.0, "ns_apply": (S - 1) / S, "ns_apply_last": 1.0 / S}
+    src = {"ns_gram": "ns_gram", "ns_poly": "ns_poly", "ns_apply": "ns_apply", "ns_apply_last": "ns_apply"}
+    half = {"ns_gram": 0.5, "ns_poly": 0.5, "ns_apply": 1.0, "ns_apply_last": 1.0}
+    fl_dense = {k: flops[src[k]] * last[k] for k in launches}
+    fl_alg = {k: fl_dense[k] * half[k] for k in launches}
+    fl_exec = {k: ex[src[k]] * last[k] for k in launches}
     kern = {}
     for k in ("ns_gram", "ns_poly", "ns_apply", "ns_apply_last"):
         if launches[k] == 0:
             continue
-        t_launch = per_step[k] / launches[k]
-        tf = fl[k] / launches[k] / (t_launch * 1e-3) / 1e12
-        kern[k] = {"ms_per_launch": t_launch, "launches_per_step": launches[k],
-                   "dense_tflops": tf, "frac_of_peak": tf / peak}
+        t = per_step[k] * 1e-3   # seconds per step in this kernel
+        rate = lambda f: f / t / 1e12
+        kern[k] = {"ms_per_launch": per_step[k] / launches[k], "launches_per_step": launches[k],
+                   "alg_tflops": rate(fl_alg[k]), "alg_frac_of_peak": rate(fl_alg[k]) / peak,
+                   "exec_tflops": rate(fl_exec[k]), "exec_frac_of_peak": rate(fl_exec[k]) / peak,
+                   "dense_equiv_tflops": rate(fl_dense[k])}
     for k in ("momentum", "update"):
         gbs = bytes_[k] / (per_step[k] * 1e-3) / 1e9
         kern[k] = {"ms": per_step[k], "gbs": gbs, "frac_of_hbm": gbs / PEAK_HBM_GBS}
     ns_ms = sum(per_step[k] for k in ("ns_gram", "ns_poly", "ns_apply", "ns_apply_last"))
     el_ms = sum(per_step[k] for k in ("momentum", "finalize", "update"))
-    ns_tflops = info.ns_dense_flops / (ns_ms * 1e-3) / 1e12
+    ns_s = ns_ms * 1e-3
+    ns_floor = floor_flops(wl.shapes, S)
+    ns_exec_tflops = info.ns_exec_flops / ns_s / 1e12
+    ns_floor_tflops = ns_floor / ns_s / 1e12
+    ns_dense_tflops = info.ns_dense_flops / ns_s / 1e12
     el_gbs = sum(bytes_.values()) / (el_ms * 1e-3) / 1e9
     alg_gbs = info.elem_bytes / (el_ms * 1e-3) / 1e9
     for k, v in per_step.items():
         log(f"  {k:13s} {v:8.3f} ms/step  {kern.get(k)}")
-    log(f"  NS total {ns_ms:.3f} ms: {ns_tflops:.1f} dense TFLOP/s ({ns_tflops / peak:.1%} of peak); "
-        f"elementwise {el_ms:.3f} ms: {el_gbs:.0f} GB/s kernel bytes, {alg_gbs:.0f} GB/s at 18 B/param")
+    log(f"  NS total {ns_ms:.3f} ms: {ns_exec_tflops:.1f} executed TFLOP/s ({ns_exec_tflops / peak:.1%} "
+        f"of peak), {ns_floor_tflops:.1f} on the method's floor ({ns_floor_tflops / peak:.1%}), "
+        f"{ns_dense_tflops:.1f} dense-equivalent; elementwise {el_ms:.3f} ms: {el_gbs:.0f} GB/s "
+        f"kernel bytes, {alg_gbs:.0f} GB/s at 18 B/param")
 
-    # The dominant kernel: the NS product with the largest share of the step.
+    # The dominant kernel: the NS product with the largest share of the step,
+    # priced on its algorithmic FLOP.
     names = {"ns_gram": "gemm_kernel<bf16, kGram> (A = X X^T)",
              "ns_poly": "gemm_kernel<bf16, kPoly> (B' = b A + c A A + a I)",
              "ns_apply": "gemm_kernel<bf16, kApply> (X' = B' X)",
              "ns_apply_last": "gemm_kernel<bf16, kApplyLast> (u = B' X)"}
+    if ns != "bf16":
+        names = {k: v.replace("<bf16", "<fp32") for k, v in names.items()}
     dom = max((k for k in kern if k in names), key=lambda k: per_step[k])
-    roof = {"bound": "mfma", "achieved": kern[dom]["dense_tflops"], "peak": peak, "unit": "TFLOP/s",
-            "frac": kern[dom]["dense_tflops"] / peak, "traffic": traffic_for(dom),
-            "kernel": names[dom], "flop_per_launch": fl[dom] / launches[dom],
+    roof = {"bound": "mfma", "achieved": kern[dom]["alg_tflops"], "peak": peak, "unit": "TFLOP/s",
+            "frac": kern[dom]["alg_tflops"] / peak, "traffic": traffic_for(dom),
+            "kernel": names[dom], "flop_per_launch": fl_alg[dom] / launches[dom],
             "ms_per_launch": kern[dom]["ms_per_launch"]}
 
     adamw = None if args.no_adamw else time_adamw(args.steps, args.warmup, dev)
@@ -358,8 +441,8 @@ def main():
 
     cpu = None
     if cpu_inputs is not None:
-        log(f"cpu baseline: oracle on {args.cpu_mats} matrices ...")
-        cpu = cpu_baseline(wl, cpu_inputs[0], cpu_inputs[1], wl.eta(0), args.cpu_mats)
+        log(f"cpu baseline: oracle on {len(cpu_idx)} matrices ...")
+        cpu = cpu_baseline(wl, cpu_inputs[0], cpu_inputs[1], wl.eta(0), cpu_idx)
         log(f"  {cpu['sample']}; {cpu['value']:.5f} steps/s on {cpu['cores']} BLAS threads")
 
     out = {
@@ -371,8 +454,14 @@ def main():
                                f"{'bf16' if gsize == 2 else 'fp32'} grads, {ns} Newton-Schulz x{S}",
                    "matrices": len(wl.shapes), "params": params, "parallelism": "single-gpu"},
         "roofline": roof,
-        "ns_dense_tflops": ns_tflops, "ns_frac_of_peak": ns_tflops / peak,
+        # NS phase rates: on the MFMA FLOP executed (the utilisation), on the
+        # method's floor 3 m^2 n + m^3 per iteration, and dense-equivalent
+        "ns_frac_of_peak": ns_exec_tflops / peak,
+        "ns_exec_tflops": ns_exec_tflops, "ns_exec_frac_of_peak": ns_exec_tflops / peak,
+        "ns_floor_tflops": ns_floor_tflops, "ns_floor_frac_of_peak": ns_floor_tflops / peak,
+        "ns_dense_equiv_tflops": ns_dense_tflops, "ns_dense_equiv_frac": ns_dense_tflops / peak,
         "ns_exec_tflop_per_step": info.ns_exec_flops / 1e12,
+        "ns_floor_tflop_per_step": ns_floor / 1e12,
         "ns_dense_tflop_per_step": info.ns_dense_flops / 1e12,
         "elementwise_gbs": el_gbs, "elementwise_frac_of_hbm": el_gbs / PEAK_HBM_GBS,
         "elementwise_alg18_gbs": alg_gbs,

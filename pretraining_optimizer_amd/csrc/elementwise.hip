@@ -27,6 +27,7 @@
 
 #include "device_util.h"
 #include "internal.h"
+#include "update_math.h"
 
 namespace muonh {
 namespace {
@@ -327,32 +328,10 @@ __global__ __launch_bounds__(64) void finalize_update_kernel(
   const double R = scal[mat].R;
   const double eta = eta_dev ? eta_dev[mat]
                              : (double)prm.elr * (elr_scale ? (double)elr_scale[mat] : 1.0);
+  const UpdateCoeffs o = update_coeffs(prm.mode, ww, wu, uu, R, eta, (double)prm.weight_decay);
   const double un = sqrt(uu), wn = sqrt(ww);
-  double k1, k2, wt_norm, elr, inner, angle = 0.0;
-  // u^ = u / ||u||; an all-zero u gives u^ = 0 (NaN still propagates: NaN != 0).
-  inner = (un != 0.0) ? wu / un : 0.0;
-  if (prm.mode == MUONH_MODE_HYPERBALL) {
-    const double k = (un != 0.0) ? eta * R / un : 0.0;   // W~ = W - k u
-    const double wt2 = ww - 2.0 * k * wu + k * k * uu;
-    wt_norm = sqrt(wt2);
-    k1 = R / wt_norm;
-    k2 = R * k / wt_norm;
-    elr = k * un / wn;
-    const double c = inner / R;
-    const double cl = fmin(1.0, fmax(-1.0, c));
-    angle = atan2(eta * sqrt(fmax(0.0, 1.0 - cl * cl)), 1.0 - eta * cl);
-  } else if (prm.mode == MUONH_MODE_MUON_WD) {
-    k1 = 1.0 - (double)prm.weight_decay * eta;
-    k2 = eta;
-    wt_norm = sqrt(fmax(0.0, k1 * k1 * ww - 2.0 * k1 * k2 * wu + k2 * k2 * uu));
-    elr = eta * un / wn;
-  } else {
-    const double eta_t = (un != 0.0) ? eta * wn / un : 0.0;
-    k1 = 1.0;
-    k2 = eta_t;
-    wt_norm = sqrt(fmax(0.0, ww - 2.0 * k2 * wu + k2 * k2 * uu));
-    elr = eta_t * un / wn;
-  }
+  const double k1 = o.k1, k2 = o.k2, wt_norm = o.wt_norm, elr = o.elr, inner = o.inner,
+               angle = o.angle;
   scal[mat].k1 = (float)k1;
   scal[mat].k2 = (float)k2;
   muonh_stats s;

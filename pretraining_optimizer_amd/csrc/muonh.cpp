@@ -374,7 +374,11 @@ struct muonh_handle {
   bool upload_pending = false;
   std::vector<MatPtrs> cur_ptrs;   // what the device pointer table holds
   bool ptrs_valid = false;
+  // The stream of the handle's last enqueued work (init, a step, a copy of
+  // u).  Work enqueued on another stream first waits for it (order_ev), so
+  // the handle's workspace is only ever used in call order.
   hipStream_t last_stream = nullptr;
+  hipEvent_t order_ev = nullptr;
   int64_t steps_done = 0;
   // timing: a ring of per-step event sets, folded into totals lazily
   static constexpr int kRing = 4;
@@ -397,6 +401,18 @@ struct muonh_handle {
 };
 
 namespace {
+
+// Orders work about to be enqueued on `st` after everything the handle
+// enqueued before (on h->last_stream), then makes `st` the last stream.
+// Every entry point that enqueues device work calls this first.
+int order_after_last(muonh_handle* h, hipStream_t st) {
+  if (st != h->last_stream) {
+    HIP_TRY(hipEventRecord(h->order_ev, h->last_stream));
+    HIP_TRY(hipStreamWaitEvent(st, h->order_ev, 0));
+    h->last_stream = st;
+  }
+  return MUONH_OK;
+}
 
 int upload_async(muonh_handle* h, void* dst, const void* src, size_t bytes, size_t staging_off,
                  hipStream_t st) {
@@ -575,7 +591,8 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
   if (hipHostMalloc(reinterpret_cast<void**>(&h->staging), h->staging_bytes, hipHostMallocDefault) !=
       hipSuccess)
     return bail(fail(MUONH_ENOMEM, "hipHostMalloc of the staging buffer failed"));
-  if (hipEventCreateWithFlags(&h->upload_done, hipEventDisableTiming) != hipSuccess)
+  if (hipEventCreateWithFlags(&h->upload_done, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->order_ev, hipEventDisableTiming) != hipSuccess)
     return bail(fail(MUONH_EHIP, "hipEventCreate failed"));
 
   // Host images of the device tables.
@@ -722,6 +739,8 @@ int prepare_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));
   if (dev != h->device) return fail(MUONH_EINVAL, "current device differs from the one at init");
+  // The workspace was last used (or initialised) on h->last_stream.
+  if ((rc = order_after_last(h, st))) return rc;
 
   // Pointer table (uploaded only when the caller's pointers change).
   std::vector<MatPtrs> ptrs(n);
@@ -921,9 +940,12 @@ int muonh_copy_update(muonh_handle* h, int32_t idx, void* dst_device, void* stre
   if (idx < 0 || idx >= h->plan.n) return fail(MUONH_EINVAL, "matrix index out of range");
   if (h->steps_done == 0) return fail(MUONH_ESTATE, "no step has run yet");
   const MatPlan& m = h->plan.mats[idx];
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // after the step that wrote u, and before any later step overwrites it
+  const int rc = order_after_last(h, st);
+  if (rc) return rc;
   const hipError_t e = launch_copy_update(h->plan.bf16 ? 1 : 0, h->ws + m.off_U, m.rows * m.cols,
-                                          reinterpret_cast<float*>(dst_device),
-                                          reinterpret_cast<hipStream_t>(stream));
+                                          reinterpret_cast<float*>(dst_device), st);
   if (e != hipSuccess) return fail(MUONH_EHIP, std::string("copy_update: ") + hipGetErrorString(e));
   return MUONH_OK;
 }
@@ -960,6 +982,7 @@ int muonh_destroy(muonh_handle* h) {
   if (h->owns_ws && h->ws) (void)hipFree(h->ws);
   if (h->staging) (void)hipHostFree(h->staging);
   if (h->upload_done) (void)hipEventDestroy(h->upload_done);
+  if (h->order_ev) (void)hipEventDestroy(h->order_ev);
   drop_graph(h);
   if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
   for (auto& set : h->ev)

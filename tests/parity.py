@@ -19,6 +19,13 @@ TOL_BF16 = 2e-2
 TOL_F32 = 1e-4
 TOL_NORM = 1e-5
 TOL_MOM = 1e-6
+# Localised-error gates on u_hat, as multiples of the Frobenius tolerance of
+# the path: the largest row (column) error relative to the RMS row (column)
+# norm, and the largest element error relative to the RMS element.  A whole
+# wrong column of a 2048 x 6144 matrix moves the Frobenius ratio by only
+# sqrt(1/6144) = 1.3e-2, but its own column error by about 1.
+ROW_COL_FACTOR = 2.0
+ELEM_FACTOR = 12.0
 
 
 def rel(a: np.ndarray, b: np.ndarray) -> float:
@@ -31,6 +38,35 @@ def unit(a: np.ndarray) -> np.ndarray:
     return a / n if n != 0 else a
 
 
+def local_errors(a: np.ndarray, b: np.ndarray):
+    """(row, col, elem) errors of a against the reference b: the largest
+    ||a_i - b_i|| over rows i divided by the RMS row norm of b, the same over
+    columns, and the largest |a_ij - b_ij| divided by the RMS element of b."""
+    d = a - b
+    nb = float(np.linalg.norm(b))
+    if nb == 0.0:
+        return 0.0, 0.0, 0.0
+    r, c = b.shape
+    row = float(np.sqrt(np.max(np.einsum("ij,ij->i", d, d)))) / (nb / math.sqrt(r))
+    col = float(np.sqrt(np.max(np.einsum("ij,ij->j", d, d)))) / (nb / math.sqrt(c))
+    elem = float(np.max(np.abs(d))) / (nb / math.sqrt(r * c))
+    return row, col, elem
+
+
+def singular_vector_agreement(u_hat: np.ndarray, svd) -> float:
+    """How far u_hat is from sharing the singular vectors of the NS input Y
+    (svd = numpy's thin SVD (U, s, V^T) of Y): the fraction of u_hat's
+    energy off the diagonal of U^T u_hat V, counting the part outside the
+    span of V, sqrt(1 - sum_i (u_i^T u_hat v_i)^2 / ||u_hat||^2).  The
+    Newton-Schulz output is U p(S) V^T exactly, for which this is 0."""
+    U, _, Vt = svd
+    d = np.einsum("ij,ij->j", U, u_hat @ Vt.T)    # u_i^T u_hat v_i
+    n2 = float(np.sum(u_hat * u_hat))
+    if n2 == 0.0:
+        return 0.0
+    return math.sqrt(max(0.0, 1.0 - float(np.sum(d * d)) / n2))
+
+
 @dataclasses.dataclass
 class StepReport:
     step: int
@@ -40,6 +76,11 @@ class StepReport:
     norm_err: List[float]     # | ||W_gpu|| / R - 1 |, ALL matrices
     stats: List[dict]
     oracle_diag: list
+    u_row: List[float] = dataclasses.field(default_factory=list)   # local_errors of u^
+    u_col: List[float] = dataclasses.field(default_factory=list)
+    u_elem: List[float] = dataclasses.field(default_factory=list)
+    checked: List[int] = dataclasses.field(default_factory=list)   # matrix index of each entry
+    sv_err: dict = dataclasses.field(default_factory=dict)        # index -> singular-vector agreement
 
 
 def announce(msg: str):
@@ -51,9 +92,16 @@ def run_parity(shapes: Sequence, make_w: Callable[[int], torch.Tensor],
                check: Sequence[int], ns: str = "bf16", oracle_opts: Optional[oracle.OracleOptions] = None,
                mode: int = pm.MUONH_MODE_HYPERBALL, weight_decay: float = 0.0,
                elr_scale: Optional[Sequence[float]] = None, radii=None, graph: bool = False,
+               check_first: Sequence[int] = (), svd_of: Optional[Callable] = None,
                **lib_opts) -> List[StepReport]:
     """make_w(i) -> fp32 CUDA tensor, make_g(step, i) -> CUDA gradient.
-    graph=True takes every step through the recorded-graph entry point."""
+    graph=True takes every step through the recorded-graph entry point.
+    The oracle follows the matrices in `check` through every step; those in
+    `check_first` are checked at the first step only, one at a time (their
+    W_0 is made again with make_w, so no host copy of the whole set is kept).
+    svd_of(i, y) -> thin SVD of matrix i's first Newton-Schulz input y, or
+    None: when given, the first step also records the singular-vector
+    agreement of every checked u_hat (StepReport.sv_err)."""
     dev = torch.device("cuda")
     oo = oracle_opts or oracle.OracleOptions()
     ws = [make_w(i).to(dev).contiguous() for i in range(len(shapes))]
@@ -79,9 +127,8 @@ def run_parity(shapes: Sequence, make_w: Callable[[int], torch.Tensor],
         torch.cuda.synchronize()
         stats = opt.stats()
         rep = StepReport(k, [], [], [], [], stats, [])
-        for i in check:
-            st = states[i]
-            g = inputs.to_numpy64(gs[i])
+
+        def compare(i, st, g, u_gpu, w_gpu, m_gpu):
             st.m = oracle.momentum_update(st.m, g, oo.beta)
             y = oracle.ns_input(st.m, g, oo.beta, oo.nesterov)
             u = oracle.newton_schulz(y, oo.ns_steps, oo.ns_coeffs, oo.ns_eps, oo.orient)
@@ -93,19 +140,75 @@ def run_parity(shapes: Sequence, make_w: Callable[[int], torch.Tensor],
             else:
                 st.w, d = oracle.elr_aligned_update(st.w, u, e)
             rep.oracle_diag.append((u, d))
-            rep.u_err.append(rel(unit(us[i]), unit(u)))
-            rep.w_err.append(rel(inputs.to_numpy64(ws[i]), st.w))
-            rep.m_err.append(rel(inputs.to_numpy64(ms[i]), st.m))
+            a, b = unit(u_gpu), unit(u)
+            rep.u_err.append(rel(a, b))
+            lr, lc, le = local_errors(a, b)
+            rep.u_row.append(lr)
+            rep.u_col.append(lc)
+            rep.u_elem.append(le)
+            rep.checked.append(i)
+            rep.w_err.append(rel(w_gpu, st.w))
+            rep.m_err.append(rel(m_gpu, st.m))
+            if svd_of is not None and k == 0:
+                sv = svd_of(i, y)
+                if sv is not None:
+                    rep.sv_err[i] = (singular_vector_agreement(a, sv), singular_vector_agreement(b, sv))
+
+        for i in check:
+            compare(i, states[i], inputs.to_numpy64(gs[i]), us[i], inputs.to_numpy64(ws[i]),
+                    inputs.to_numpy64(ms[i]))
+        if k == 0:
+            for i in check_first:
+                if i in states:
+                    continue
+                st = oracle.OracleMatrixState.from_arrays(
+                    inputs.to_numpy64(make_w(i)), R=None if radii is None else radii[i])
+                if radii is None:
+                    assert abs(R[i] / st.R - 1.0) < 1e-6, (i, R[i], st.R)
+                u_gpu = inputs.to_numpy64(opt.copy_update(i))
+                compare(i, st, inputs.to_numpy64(gs[i]), u_gpu, inputs.to_numpy64(ws[i]),
+                        inputs.to_numpy64(ms[i]))
+                rep.oracle_diag[-1] = None   # drop the fp64 u of a matrix not followed further
+                del st, u_gpu
         if mode == pm.MUONH_MODE_HYPERBALL:
             for i, w in enumerate(ws):
                 wn = torch.linalg.vector_norm(w.double()).item()
                 rep.norm_err.append(abs(wn / R[i] - 1.0))
         reports.append(rep)
-        announce(f"step {k}: max u^ err {max(rep.u_err):.3e}, max W err {max(rep.w_err):.3e}, "
-                 f"max M err {max(rep.m_err):.3e}, max |W|/R-1 "
+        announce(f"step {k}: {len(rep.u_err)} matrices checked; max u^ err {max(rep.u_err):.3e} "
+                 f"(row {max(rep.u_row):.3e}, col {max(rep.u_col):.3e}, elem {max(rep.u_elem):.3e}), "
+                 f"max W err {max(rep.w_err):.3e}, max M err {max(rep.m_err):.3e}, max |W|/R-1 "
                  f"{max(rep.norm_err) if rep.norm_err else float('nan'):.2e}")
+        if rep.sv_err:
+            g_sv = max(v[0] for v in rep.sv_err.values())
+            o_sv = max(v[1] for v in rep.sv_err.values())
+            announce(f"step {k}: singular-vector agreement (off-diagonal energy of U^T u^ V): "
+                     f"library max {g_sv:.3e}, oracle max {o_sv:.3e}")
     opt.close()
     return reports
+
+
+def summarize(name: str, reports: List[StepReport]) -> dict:
+    """Largest errors over all steps and checked matrices, announced and, when
+    MUONH_PARITY_LOG names a file, appended to it as one JSON line (the
+    margins under each gate)."""
+    import json
+    import os
+    out = {"case": name, "steps": len(reports),
+           "matrices_checked_first_step": len(reports[0].u_err) if reports else 0}
+    for key in ("u_err", "u_row", "u_col", "u_elem", "w_err", "m_err", "norm_err"):
+        vals = [v for r in reports for v in getattr(r, key)]
+        out[key] = max(vals) if vals else None
+    sv = [v for r in reports for v in r.sv_err.values()]
+    if sv:
+        out["sv_lib"] = max(v[0] for v in sv)
+        out["sv_oracle"] = max(v[1] for v in sv)
+    announce("summary " + json.dumps(out))
+    path = os.environ.get("MUONH_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(out) + "\n")
+    return out
 
 
 def workload_fns(wl: inputs.Workload, device="cuda"):
@@ -119,6 +222,9 @@ def check_reports(reports: List[StepReport], tol_u: float, etas: Sequence[float]
     for rep, eta in zip(reports, etas):
         acc += abs(eta)
         assert max(rep.u_err) <= tol_u, (rep.step, rep.u_err)
+        assert max(rep.u_row) <= ROW_COL_FACTOR * tol_u, (rep.step, "row", rep.u_row)
+        assert max(rep.u_col) <= ROW_COL_FACTOR * tol_u, (rep.step, "col", rep.u_col)
+        assert max(rep.u_elem) <= ELEM_FACTOR * tol_u, (rep.step, "elem", rep.u_elem)
         assert max(rep.m_err) <= TOL_MOM, (rep.step, rep.m_err)
         # W moves by eta*R*u^ per step, so its error is bounded by the
         # accumulated step sizes times the u^ tolerance (plus fp32 rounding).

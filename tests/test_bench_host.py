@@ -40,6 +40,32 @@ def test_work_model_matches_plan():
     assert b2["momentum"] == pytest.approx(10.0 * p2 + 2.0 * 256 * 512)
 
 
+def test_executed_and_floor_flop_models_match_the_plan(monkeypatch):
+    """bench.py splits the plan's executed MFMA FLOP per product; the split
+    must add up to what the library plans, on both GEMM paths."""
+    for name, ns in (("qwen3_1.7b", pm.MUONH_BF16), ("stress", pm.MUONH_BF16),
+                     ("stress", pm.MUONH_F32), ("diag170m", pm.MUONH_BF16)):
+        wl = inputs.workload(name)
+        tsize = 2 if ns == pm.MUONH_BF16 else 4
+        info = pm.plan_query(wl.shapes, pm.default_options(ns_dtype=ns))
+        ex = bench.plan_exec_flops(wl.shapes, 5, tsize, info.ns_exec_flops)
+        assert sum(ex.values()) == pytest.approx(info.ns_exec_flops, rel=1e-12)
+    # the single 256 x 128 matrix runs on the 64 x 64 path
+    info = pm.plan_query([(256, 128)], pm.default_options(ns_dtype=pm.MUONH_F32), g_dtype=pm.MUONH_F32)
+    assert sum(bench.exec_flops([(256, 128)], 5, 4, True).values()) == pytest.approx(info.ns_exec_flops)
+    monkeypatch.setenv("MUONH_GEMM_TILE", "256")
+    info = pm.plan_query([(256, 128)], pm.default_options(ns_dtype=pm.MUONH_F32), g_dtype=pm.MUONH_F32)
+    assert sum(bench.exec_flops([(256, 128)], 5, 4, False).values()) == pytest.approx(info.ns_exec_flops)
+    # aligned 1.7B shapes: the floor is 3 m^2 n + m^3 per iteration; the
+    # executed count lies between it and the dense one (the diagonal tiles)
+    wl = inputs.workload("qwen3_1.7b")
+    f, _, _ = bench.per_kernel_work(wl.shapes, 5, 2, 2)
+    floor = bench.floor_flops(wl.shapes, 5)
+    assert floor == pytest.approx(f["ns_gram"] / 2 + f["ns_poly"] / 2 + f["ns_apply"], rel=1e-12)
+    info = pm.plan_query(wl.shapes)
+    assert floor < info.ns_exec_flops < sum(f.values())
+
+
 def _copy_sources(dst):
     src = os.path.join(ROOT, "pretraining_optimizer_amd", "csrc")
     out = os.path.join(dst, "pretraining_optimizer_amd", "csrc")

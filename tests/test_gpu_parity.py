@@ -15,8 +15,8 @@ import torch
 import inputs
 import oracle
 import pretraining_optimizer_amd as pm
-from parity import (TOL_BF16, TOL_F32, TOL_NORM, announce, check_reports, rel, run_parity, unit,
-                    workload_fns)
+from parity import (TOL_BF16, TOL_F32, TOL_NORM, announce, check_reports, rel, run_parity,
+                    summarize, unit, workload_fns)
 
 pytestmark = pytest.mark.gpu
 
@@ -47,6 +47,7 @@ def test_single_fp32_trajectory(tile, monkeypatch):
     etas = [wl.eta(k) for k in range(wl.steps)]
     mw, mg = workload_fns(wl)
     reps = run_parity(wl.shapes, mw, mg, etas, check=[0], ns="f32")
+    summarize(f"single fp32, tile {tile}", reps)
     check_reports(reps, TOL_F32, etas)
 
 
@@ -63,43 +64,57 @@ def test_ragged_shapes(ns, tol, tile, monkeypatch):
     mw, mg = _gauss_fns(RAGGED, torch.bfloat16 if ns == "bf16" else torch.float32, seed=1)
     etas = [0.02, 0.015]
     reps = run_parity(RAGGED, mw, mg, etas, check=list(range(len(RAGGED))), ns=ns)
+    summarize(f"ragged {ns}, tile {tile}", reps)
     check_reports(reps, tol, etas)
+
+
+# Thin SVDs of the stress set's first Newton-Schulz inputs (Y = M_1 = G_0),
+# shared by the fp32 and bf16 runs of the stress tests.
+_STRESS_SVD = {}
+
+
+def _stress_svd(i, y):
+    if i not in _STRESS_SVD:
+        _STRESS_SVD[i] = np.linalg.svd(y, full_matrices=False)
+    return _STRESS_SVD[i]
 
 
 @pytest.mark.parametrize("ns,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
 def test_stress_set_trajectory(ns, tol):
-    """All 64 stress matrices in one grouped launch, 3 steps at eta 0.02; the
-    oracle follows a subset (matrices are independent, so each followed one
-    is an exact check): the 8 smallest, the 2 largest and the 2 most
-    elongated of each orientation."""
-    announce(f"stress set, ns {ns}, 3 steps")
+    """All 64 stress matrices (aspect 1:1 to 1:8, sides 128-4096, rank-8
+    signal with singular values 10^U(-3,1) plus noise) in one grouped launch,
+    3 steps at eta 0.02, every matrix followed by the oracle at every step.
+    The first step also measures how well u_hat keeps the singular vectors
+    of the Newton-Schulz input (off-diagonal energy of U^T u_hat V from the
+    SVD of Y): the library's value is gated like u_hat itself, the oracle's
+    must vanish to fp64 rounding."""
+    announce(f"stress set, ns {ns}, 3 steps, all 64 matrices")
     wl = inputs.workload("stress")
     mw, mg = workload_fns(wl)
-    sizes = [r * c for r, c in wl.shapes]
-    order = np.argsort(sizes)
-    aspect = np.array([r / c for r, c in wl.shapes])
-    ar = np.argsort(aspect)
-    check = sorted(set(order[:8].tolist() + order[-2:].tolist() + ar[:2].tolist() + ar[-2:].tolist()))
     etas = [wl.eta(k) for k in range(wl.steps)]
-    reps = run_parity(wl.shapes, mw, mg, etas, check=check, ns=ns)
+    reps = run_parity(wl.shapes, mw, mg, etas, check=list(range(len(wl.shapes))), ns=ns,
+                      svd_of=_stress_svd)
+    out = summarize(f"stress {ns}, 3 steps", reps)
     check_reports(reps, tol, etas)
+    sv = reps[0].sv_err
+    assert len(sv) == len(wl.shapes)
+    for i, (lib, ora) in sv.items():
+        assert lib <= tol, (i, lib)
+        assert ora <= 1e-9, (i, ora)
+    announce(f"stress {ns}: singular-vector agreement max {out['sv_lib']:.3e} "
+             f"(oracle {out['sv_oracle']:.1e}) over {len(sv)} matrices")
 
 
 @pytest.mark.parametrize("ns,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
 def test_stress_set_small_gemm_path(ns, tol, monkeypatch):
     """The 64 stress matrices (dims 128-4096, ragged) forced onto the
-    small-problem GEMM path, one step; the oracle follows the same subset as
-    the trajectory test."""
+    small-problem GEMM path, one step, every matrix checked."""
     monkeypatch.setenv("MUONH_GEMM_TILE", "64")
     announce(f"stress set on the 64 x 64 GEMM path, ns {ns}, 1 step")
     wl = inputs.workload("stress")
     mw, mg = workload_fns(wl)
-    sizes = [r * c for r, c in wl.shapes]
-    order = np.argsort(sizes)
-    aspect = np.array([r / c for r, c in wl.shapes])
-    ar = np.argsort(aspect)
-    check = sorted(set(order[:8].tolist() + order[-2:].tolist() + ar[:2].tolist() + ar[-2:].tolist()))
-    reps = run_parity(wl.shapes, mw, mg, [wl.eta(0)], check=check, ns=ns)
+    reps = run_parity(wl.shapes, mw, mg, [wl.eta(0)], check=list(range(len(wl.shapes))), ns=ns)
+    summarize(f"stress {ns}, 64-tile path", reps)
     check_reports(reps, tol, [wl.eta(0)])
 
 
@@ -113,6 +128,7 @@ def test_maximum_dimension(ns, tol, tile, monkeypatch):
     shapes = [(65536, 96), (100, 65536)]
     mw, mg = _gauss_fns(shapes, torch.bfloat16 if ns == "bf16" else torch.float32, seed=21)
     reps = run_parity(shapes, mw, mg, [0.02], check=[0, 1], ns=ns)
+    summarize(f"max dimension {ns}, tile {tile}", reps)
     check_reports(reps, tol, [0.02])
 
 
@@ -160,25 +176,33 @@ def test_rank_one_gradient_gives_its_outer_product(ns, tile, monkeypatch):
 
 def test_diag170m_trajectory():
     """170M-class set (84 matrices, bf16 grads scaled by 1/sqrt(fan_in)), all 20
-    steps of the linear ELR decay; the oracle follows layers 0 and 11."""
+    steps of the linear ELR decay; the oracle checks every matrix at the first
+    step and follows layers 0 and 11 through all 20."""
     announce("diag170m, 20 steps")
     wl = inputs.workload("diag170m")
     mw, mg = workload_fns(wl)
     etas = [wl.eta(k) for k in range(wl.steps)]
     check = list(range(7)) + list(range(77, 84))
-    reps = run_parity(wl.shapes, mw, mg, etas, check=check, ns="bf16")
+    reps = run_parity(wl.shapes, mw, mg, etas, check=check, ns="bf16",
+                      check_first=range(len(wl.shapes)))
+    summarize("diag170m bf16, 20 steps", reps)
     check_reports(reps, TOL_BF16, etas)
+    assert len(reps[0].u_err) == 84
 
 
 def test_qwen3_06b_trajectory():
     """Qwen3-0.6B set (196 matrices), all 10 steps of the linear decay from
-    0.024; the oracle follows the seven matrices of layer 0."""
+    0.024; the oracle checks all 196 matrices at the first step and follows
+    the seven of layer 0 through all 10."""
     announce("qwen3-0.6b set, 10 steps")
     wl = inputs.workload("qwen3_0.6b")
     mw, mg = workload_fns(wl)
     etas = [wl.eta(k) for k in range(wl.steps)]
-    reps = run_parity(wl.shapes, mw, mg, etas, check=list(range(7)), ns="bf16")
+    reps = run_parity(wl.shapes, mw, mg, etas, check=list(range(7)), ns="bf16",
+                      check_first=range(len(wl.shapes)))
+    summarize("qwen3_0.6b bf16, 10 steps", reps)
     check_reports(reps, TOL_BF16, etas)
+    assert len(reps[0].u_err) == 196
 
 
 def test_qwen3_17b_full_size():
@@ -186,27 +210,49 @@ def test_qwen3_17b_full_size():
     same launch configuration the benchmark times, all 10 steps; the oracle
     follows all seven matrices of layer 0 and q, k, v, o of layers 13 and 27
     (each an exact check, matrices being independent), and the norm
-    invariant is checked on all 196 matrices after every step."""
+    invariant is checked on all 196 matrices after every step.  Every other
+    matrix is checked at the first step by test_qwen3_17b_every_matrix."""
     announce("qwen3-1.7b full set, 10 steps")
     wl = inputs.workload("qwen3_1.7b")
     mw, mg = workload_fns(wl)
     etas = [wl.eta(k) for k in range(wl.steps)]
     check = list(range(7)) + [7 * l + j for l in (13, 27) for j in range(4)]
     reps = run_parity(wl.shapes, mw, mg, etas, check=check, ns="bf16")
+    summarize("qwen3_1.7b bf16, 10 steps, followed subset", reps)
     check_reports(reps, TOL_BF16, etas)
     for rep in reps:
         assert len(rep.norm_err) == 196
 
 
-def test_qwen3_17b_fp32_newton_schulz():
-    """The benchmarked 1.7B set with the fp32 Newton-Schulz path (fp32 MFMA,
-    X and X^T both stored), 2 steps; the oracle follows layer 0 to the fp32
-    tolerance and the norm invariant is checked on all 196 matrices."""
-    announce("qwen3-1.7b full set, fp32 Newton-Schulz, 2 steps")
+@pytest.mark.parametrize("layers", [(0, 7), (7, 14), (14, 21), (21, 28)])
+def test_qwen3_17b_every_matrix(layers):
+    """The first step of the benchmarked 1.7B set (all 196 matrices in one
+    grouped launch per product, as the benchmark runs it), with the oracle
+    checking every matrix of seven layers: together the four cases cover
+    all 196, including gate, up and down beyond layer 0 (whose tiles sit at
+    other positions of the tile lists and other partial-slot offsets)."""
+    l0, l1 = layers
+    announce(f"qwen3-1.7b full set, first step, layers {l0}-{l1 - 1}")
     wl = inputs.workload("qwen3_1.7b")
     mw, mg = workload_fns(wl)
-    etas = [wl.eta(k) for k in range(2)]
-    reps = run_parity(wl.shapes, mw, mg, etas, check=list(range(7)), ns="f32")
+    reps = run_parity(wl.shapes, mw, mg, [wl.eta(0)], check=[], ns="bf16",
+                      check_first=range(7 * l0, 7 * l1))
+    summarize(f"qwen3_1.7b bf16, first step, layers {l0}-{l1 - 1}", reps)
+    check_reports(reps, TOL_BF16, [wl.eta(0)])
+    assert len(reps[0].u_err) == 7 * (l1 - l0) and len(reps[0].norm_err) == 196
+
+
+def test_qwen3_17b_fp32_newton_schulz():
+    """The benchmarked 1.7B set with the fp32 Newton-Schulz path (fp32 MFMA,
+    X and X^T both stored), all 10 steps; the oracle follows the seven
+    matrices of layers 0 and 27 to the fp32 tolerance and the norm invariant
+    is checked on all 196 matrices."""
+    announce("qwen3-1.7b full set, fp32 Newton-Schulz, 10 steps")
+    wl = inputs.workload("qwen3_1.7b")
+    mw, mg = workload_fns(wl)
+    etas = [wl.eta(k) for k in range(wl.steps)]
+    reps = run_parity(wl.shapes, mw, mg, etas, check=list(range(7)) + list(range(189, 196)), ns="f32")
+    summarize("qwen3_1.7b fp32, 10 steps, layers 0 and 27", reps)
     check_reports(reps, TOL_F32, etas)
     for rep in reps:
         assert len(rep.norm_err) == 196
@@ -215,12 +261,13 @@ def test_qwen3_17b_fp32_newton_schulz():
 def test_qwen3_17b_fused_projections():
     """Qwen3-1.7B dims with fused qkv (4096 x 2048) and gate_up (12288 x 2048)
     matrices: wider Newton-Schulz problems (n up to 12288) in the same grouped
-    launches; the oracle checks the four matrices of layer 0."""
+    launches; the oracle checks the four matrices of layers 0 and 27."""
     announce("qwen3-1.7b fused projections, 1 step")
     wl = inputs.workload("qwen3_1.7b_fused")
     mw, mg = workload_fns(wl)
     etas = [wl.eta(0)]
-    reps = run_parity(wl.shapes, mw, mg, etas, check=list(range(4)), ns="bf16")
+    reps = run_parity(wl.shapes, mw, mg, etas, check=list(range(4)) + list(range(108, 112)), ns="bf16")
+    summarize("qwen3_1.7b_fused bf16, first step, layers 0 and 27", reps)
     check_reports(reps, TOL_BF16, etas)
     for rep in reps:
         assert len(rep.norm_err) == 112
@@ -305,20 +352,29 @@ def test_symmetric_and_full_tiles_agree(monkeypatch):
 
 
 @pytest.mark.parametrize("tile", ["auto", "256"])
+@pytest.mark.parametrize("ns,tol", [("f32", TOL_F32), ("bf16", TOL_BF16)])
 @pytest.mark.parametrize("mode", [pm.MUONH_MODE_MUON_WD, pm.MUONH_MODE_ELR_ALIGNED])
-def test_other_update_modes(mode, tile, monkeypatch):
+def test_other_update_modes(mode, ns, tol, tile, monkeypatch):
     """Ordinary Muon with decoupled weight decay (Eq. 3) and ELR-aligned Muon
-    (Eq. 5), on the plan's own GEMM path and on the 256 x 256 one."""
+    (Eq. 5), with fp32 and bf16 Newton-Schulz, on the plan's own GEMM path
+    and on the 256 x 256 one.  Both updates are linear in u, so W's error is
+    at most the step size times u's (plus fp32 rounding of W)."""
     if tile != "auto":
         monkeypatch.setenv("MUONH_GEMM_TILE", tile)
-    announce(f"mode {mode}, GEMM tile {tile}")
+    announce(f"mode {mode}, ns {ns}, GEMM tile {tile}")
     shapes = [(256, 384), (640, 256)]
-    mw, mg = _gauss_fns(shapes, torch.float32, seed=4)
+    gdt = torch.float32 if ns == "f32" else torch.bfloat16
+    mw, mg = _gauss_fns(shapes, gdt, seed=4)
     etas = [0.02, 0.01]
-    reps = run_parity(shapes, mw, mg, etas, check=[0, 1], ns="f32", mode=mode, weight_decay=0.1)
+    reps = run_parity(shapes, mw, mg, etas, check=[0, 1], ns=ns, mode=mode, weight_decay=0.1)
+    summarize(f"mode {mode} {ns}, tile {tile}", reps)
+    acc = 0.0
     for rep in reps:
-        assert max(rep.u_err) <= TOL_F32
-        assert max(rep.w_err) <= 1e-5
+        acc += etas[rep.step]
+        assert max(rep.u_err) <= tol
+        # Eq. (3): W moves by eta u, |u| = ||u^|| sqrt(rows) scale; Eq. (5):
+        # by eta ||W|| u^.  Relative to ||W|| both are O(eta) times u^'s error.
+        assert max(rep.w_err) <= 2.0 * acc * tol + 1e-5, (rep.step, rep.w_err)
         if mode == pm.MUONH_MODE_ELR_ALIGNED:
             for s, eta in zip(rep.stats, etas):
                 assert s["elr"] == pytest.approx(etas[rep.step], rel=1e-5)
@@ -534,5 +590,38 @@ def test_steps_on_a_side_stream():
         torch.cuda.synchronize()
         opt.close()
         outs.append([w.clone() for w in ws] + [m.clone() for m in ms])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+
+
+def test_init_on_a_side_stream_then_steps_on_the_current_one():
+    """The handle orders its own work across streams: init (workspace
+    clearing, radius kernels) enqueued on a side stream, then steps and
+    copies of u on torch's current stream with no synchronisation in
+    between, then a copy of u on the side stream after a step on the current
+    one, give bitwise the results of doing everything on one stream."""
+    announce("init on a side stream, steps on the current stream")
+    shapes = [(512, 768), (1000, 260)]
+    mw, mg = _gauss_fns(shapes, torch.bfloat16, seed=12)
+    outs = []
+    for mixed in (False, True):
+        ws = [mw(i).cuda() for i in range(len(shapes))]
+        ms = [torch.zeros_like(w) for w in ws]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())   # W and M are ready
+        opt = pm.MuonH(ws, ms, grad_dtype=torch.bfloat16, stream=side if mixed else None)
+        us = []
+        for k in range(3):
+            opt.step([mg(k, i).cuda() for i in range(len(shapes))], 0.02)
+            if mixed and k == 1:
+                u = opt.copy_update(0, stream=side)   # ordered after the step by the library
+                torch.cuda.current_stream().wait_stream(side)
+            else:
+                u = opt.copy_update(0)
+            us.append(u)
+        torch.cuda.synchronize()
+        R = opt.radii()
+        opt.close()
+        outs.append([w.clone() for w in ws] + [m.clone() for m in ms] + us + [torch.tensor(R)])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
