@@ -55,16 +55,21 @@ def local_errors(a: np.ndarray, b: np.ndarray):
 
 def singular_vector_agreement(u_hat: np.ndarray, svd) -> float:
     """How far u_hat is from sharing the singular vectors of the NS input Y
-    (svd = numpy's thin SVD (U, s, V^T) of Y): the fraction of u_hat's
-    energy off the diagonal of U^T u_hat V, counting the part outside the
-    span of V, sqrt(1 - sum_i (u_i^T u_hat v_i)^2 / ||u_hat||^2).  The
-    Newton-Schulz output is U p(S) V^T exactly, for which this is 0."""
+    (svd = numpy's thin SVD (U, s, V^T) of Y): with C = U^T u_hat V, the
+    energy of u_hat off the diagonal of C plus the energy outside the spans
+    of U and V, over ||u_hat||:
+        sqrt(||C - diag(C)||^2 + ||u_hat - U C V^T||^2) / ||u_hat||.
+    The Newton-Schulz output is U p(S) V^T exactly, for which this is 0.
+    Both terms are formed directly (not as ||u_hat||^2 - ||diag C||^2, whose
+    cancellation floors the measure at about 1e-8)."""
     U, _, Vt = svd
-    d = np.einsum("ij,ij->j", U, u_hat @ Vt.T)    # u_i^T u_hat v_i
-    n2 = float(np.sum(u_hat * u_hat))
-    if n2 == 0.0:
+    n = float(np.linalg.norm(u_hat))
+    if n == 0.0:
         return 0.0
-    return math.sqrt(max(0.0, 1.0 - float(np.sum(d * d)) / n2))
+    C = U.T @ u_hat @ Vt.T
+    off = C - np.diag(np.diag(C))
+    rest = u_hat - U @ C @ Vt
+    return math.sqrt(float(np.sum(off * off)) + float(np.sum(rest * rest))) / n
 
 
 @dataclasses.dataclass
