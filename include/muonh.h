@@ -174,6 +174,37 @@ int muonh_step(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
 int muonh_step_graph(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
                      const muonh_step_args* args, void* stream);
 
+/* Allocation-free variant of muonh_step, for callers that cannot allocate
+ * device memory: code that must not call hipMalloc or hipFree (tight serving
+ * or training loops, harnesses that forbid allocation).  One self-contained
+ * step over n matrices with no handle: the plan is built on the host each
+ * call, and every buffer the step needs beyond the caller's W, G and M
+ * (tables, Newton-Schulz iterates, partial sums) lives in one static device
+ * array of the library, MUONH_NOALLOC_MAX_WORKSPACE bytes per GPU, which
+ * each GPU the library runs on holds until the process ends.  No device
+ * memory is allocated or freed and no pinned host memory is used (the
+ * tables are uploaded from a host buffer the library reuses; the host-side
+ * plan uses the C++ heap).  The first call on a device looks up that
+ * device's address of the array.
+ *   mats, n, args, stream: as for muonh_step (pointers, shapes, dtypes);
+ *     every desc.radius must be > 0: the caller holds R (||W_0||_F, or the
+ *     value muonh_get_radii returns), since nothing persists between calls.
+ *   opt: as for muonh_init; opt->workspace must be NULL.
+ * Same plan, kernels and launch order as muonh_init + muonh_step with the
+ * same options and radii: W and M come out bitwise equal.  Statistics and u
+ * are not kept for the caller.
+ * Errors: MUONH_EINVAL (as muonh_step, or a radius <= 0, or a workspace
+ * given); MUONH_ENOMEM when the list's plan (muonh_workspace_size) exceeds
+ * MUONH_NOALLOC_MAX_WORKSPACE, before anything is enqueued; MUONH_ENODEV;
+ * MUONH_EHIP.  Every call on a GPU shares that GPU's array, which keeps the
+ * last call's contents (each call uploads its own tables and clears the
+ * Newton-Schulz buffers): calls that overlap in time on one GPU, on other
+ * streams or from other threads, race; calls in order on one stream do
+ * not.                                                                     */
+#define MUONH_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+int muonh_step_noalloc(const muonh_matrix_desc* mats, int32_t n, const muonh_options* opt,
+                       const muonh_step_args* args, void* stream);
+
 /* Synchronise the handle's last stream, then copy the n radii to host.  A
  * radius measured at init is rounded to float when measured, so these are
  * exactly the R the steps use: a new handle given them as the descriptors'

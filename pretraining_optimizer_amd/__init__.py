@@ -11,10 +11,12 @@ from .muonh import (  # noqa: F401
     AdamW,
     MuonH,
     MuonHError,
+    NOALLOC_MAX_WORKSPACE,
     adamw_default_options,
     default_options,
     load_library,
     plan_query,
+    step_noalloc,
     workspace_size,
     MUONH_BF16,
     MUONH_F32,

@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmuonh.so")
-SOURCES = ("muonh.cpp", "adamw.cpp", "gemm.hip", "elementwise.hip")
+SOURCES = ("muonh.cpp", "adamw.cpp", "gemm.hip", "elementwise.hip", "noalloc.hip")
 ARCH = "gfx950"
 
 

@@ -25,6 +25,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "device_util.h"
 #include "internal.h"
 #include "update_math.h"
@@ -395,6 +397,17 @@ __global__ __launch_bounds__(kElemThreads) void update_kernel(const Chunk* __res
   }
 }
 
+// Zero fill of a 16-byte aligned region whose size is a multiple of 16 bytes
+// (clears the Newton-Schulz buffers of a workspace that other plans used
+// before; a kernel rather than a memset so a captured graph holds no memset
+// node).  One 16-byte store per thread and iteration, grid-stride.
+__global__ __launch_bounds__(kElemThreads) void fill_zero_kernel(u32x4_t* __restrict__ p, int64_t n16) {
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  for (int64_t i = (int64_t)blockIdx.x * kElemThreads + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * kElemThreads)
+    p[i] = z;
+}
+
 // ||W_0||^2 partials (radius at init).
 __global__ __launch_bounds__(kElemThreads) void radius_kernel(const Chunk* __restrict__ chunks,
                                                               const MatPtrs* __restrict__ ptrs,
@@ -584,6 +597,16 @@ hipError_t launch_finalize_radius(int32_t nmat, const MatGeom* geo, const double
                                   const int32_t* need, MatScalars* scal, hipStream_t st) {
   hipLaunchKernelGGL(finalize_radius_kernel, dim3(nmat), dim3(64), 0, st, geo, partials, need,
                      scal);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+  if (bytes == 0) return hipSuccess;
+  if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0 || (bytes & 15u) != 0) return hipErrorInvalidValue;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const int64_t blocks = std::min<int64_t>((n16 + kElemThreads - 1) / kElemThreads, 4096);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(kElemThreads), 0, st,
+                     reinterpret_cast<u32x4_t*>(p), n16);
   return hipGetLastError();
 }
 

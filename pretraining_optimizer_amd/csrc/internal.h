@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "../../include/muonh.h"
 
 namespace muonh {
@@ -174,6 +176,9 @@ hipError_t launch_finalize_radius(int32_t nmat, const MatGeom* geo, const double
 
 hipError_t launch_copy_update(int bf16, const void* U, int64_t count, float* dst, hipStream_t st);
 
+// Zero fill of a 16-byte aligned region of `bytes` (a multiple of 16).
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
 // AdamW over a list of flat tensors (chunks of kChunk elements).
 struct AdamwPtrs {
   float* w;
@@ -196,5 +201,25 @@ hipError_t launch_adamw(const Chunk* chunks, int64_t nchunks, const AdamwPtrs* p
 
 // Records the text of a failure for muonh_last_error() and returns `code`.
 int set_last_error(int code, const char* msg);
+
+// Host state one device keeps for the allocation-free step: the host image
+// of the plan tables (reused, so an upload's source stays valid until the
+// device has read it) and the event recorded after that upload.
+struct InWorkspaceHost {
+  std::vector<uint8_t> img;    // host image of the tables (C++ heap, grown on demand)
+  hipEvent_t uploaded = nullptr;
+  bool pending = false;
+};
+
+// One MuonH step over `mats` with every buffer the step needs beyond the
+// caller's W, G and M inside the device region [ws, ws + ws_bytes): the plan
+// is built on the host, its tables uploaded into the region, the
+// Newton-Schulz buffers cleared, and the step's launches enqueued on `st`,
+// with no device allocation.  Every radius must be given (> 0).  Errors:
+// MUONH_EINVAL, MUONH_ENOMEM (the plan needs more than ws_bytes; the text
+// names the size), MUONH_EHIP.
+int run_step_in_workspace(const muonh_matrix_desc* mats, int32_t n, const muonh_options& opt,
+                          const muonh_step_args& args, hipStream_t st, uint8_t* ws, size_t ws_bytes,
+                          InWorkspaceHost& host);
 
 }  // namespace muonh

@@ -357,6 +357,121 @@ int build_plan(const muonh_matrix_desc* mats, int32_t n, const muonh_options& op
   return MUONH_OK;
 }
 
+// Host image of the workspace's table region [0, pl.off_part_mom) for a
+// workspace at device address `ws`: geometry, radii (R where given, else 0
+// with need = 1), zeroed statistics and step-size slots, the momentum units,
+// chunk and tile lists, the GEMM problem descriptors and, when `mats` carries
+// pointers (any w non-null), the pointer table.  The partial-sum slots that
+// follow are rewritten by every step before they are read.
+void build_table_image(const Plan& pl, uint8_t* ws, const muonh_matrix_desc* mats,
+                       std::vector<uint8_t>& img, std::vector<int32_t>& need) {
+  const int32_t n = pl.n;
+  img.assign(pl.off_part_mom, 0);
+  need.assign(n, 0);
+  auto put = [&](size_t off, const void* src, size_t bytes) {
+    if (bytes) std::memcpy(img.data() + off, src, bytes);
+  };
+  std::vector<MatGeom> geo(n);
+  std::vector<MatScalars> scal(n);
+  std::vector<GemmProb> gram[2], poly(n), apply[2];
+  for (int k = 0; k < 2; ++k) {
+    gram[k].resize(n);
+    apply[k].resize(n);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const MatPlan& m = pl.mats[i];
+    MatGeom& g = geo[i];
+    g.rows = m.rows;
+    g.cols = m.cols;
+    g.tall = m.tall;
+    g.g_bf16 = m.g_bf16;
+    g.m_pad = (int32_t)m.m_pad;
+    g.n_pad = (int32_t)m.n_pad;
+    g.r_pad = (int32_t)(m.tall ? m.n_pad : m.m_pad);
+    g.c_pad = (int32_t)(m.tall ? m.m_pad : m.n_pad);
+    g.ld_skew = (int32_t)(kRowSkewBytes / pl.tsize);
+    for (int k = 0; k < 2; ++k) {
+      g.X[k] = ws + m.off_X[k];
+      g.XT[k] = m.off_XT[k] == kNoBuffer ? nullptr : ws + m.off_XT[k];
+    }
+    g.U = ws + m.off_U;
+    g.mom_tile0 = m.mom_tile0;
+    g.mom_ntiles = m.mom_ntiles;
+    g.chunk0 = m.chunk0;
+    g.nchunks = m.nchunks;
+    g.part0 = m.part0;
+    g.nparts = m.nparts;
+    scal[i] = MatScalars{m.radius_in > 0.0f ? (double)m.radius_in : 0.0, 0.0, 1.0f, 1.0f, 0.0f, 0.0f};
+    need[i] = m.radius_in > 0.0f ? 0 : 1;
+    const int32_t M = (int32_t)m.m_pad, N = (int32_t)m.n_pad;
+    const int32_t LM = M + g.ld_skew, LN = N + g.ld_skew;   // row pitches
+    for (int k = 0; k < 2; ++k) {
+      GemmProb& a = gram[k][i];
+      std::memset(&a, 0, sizeof(a));
+      a.P = a.Q = g.X[k];
+      a.O = ws + m.off_A;
+      a.M = a.N = M;
+      a.K = N;
+      a.ldp = a.ldq = LN;
+      a.ldo = LM;
+      a.um = a.un = (int32_t)m.m;
+      a.uk = (int32_t)m.n;
+      a.mat = i;
+      GemmProb& c = apply[k][i];
+      std::memset(&c, 0, sizeof(c));
+      c.P = ws + m.off_B;
+      c.Q = g.XT[k] ? g.XT[k] : g.X[k];   // bf16: X itself, read K-major
+      c.E = nullptr;
+      c.O = g.X[k ^ 1];
+      c.OT = g.XT[k ^ 1];
+      c.U = g.U;
+      c.M = M;
+      c.N = N;
+      c.K = M;
+      c.ldp = LM;
+      c.ldq = g.XT[k] ? LM : LN;
+      c.lde = LM;
+      c.ldo = LN;
+      c.ldot = LM;
+      c.um = (int32_t)m.m;
+      c.un = (int32_t)m.n;
+      c.uk = (int32_t)m.m;
+      c.u_tall = m.tall;
+      c.mat = i;
+      c.part0 = (int32_t)m.part0;
+    }
+    GemmProb& b = poly[i];
+    std::memset(&b, 0, sizeof(b));
+    b.P = b.Q = b.E = ws + m.off_A;
+    b.O = ws + m.off_B;
+    b.M = b.N = b.K = M;
+    b.ldp = b.ldq = b.lde = b.ldo = LM;
+    b.um = b.un = b.uk = (int32_t)m.m;
+    b.mat = i;
+  }
+  put(pl.off_geo, geo.data(), sizeof(MatGeom) * n);
+  put(pl.off_scal, scal.data(), sizeof(MatScalars) * n);
+  put(pl.off_need, need.data(), sizeof(int32_t) * n);
+  put(pl.off_mom_tiles, pl.mom_tiles.data(), sizeof(MomTile) * pl.mom_tiles.size());
+  put(pl.off_chunks, pl.chunks.data(), sizeof(Chunk) * pl.chunks.size());
+  put(pl.off_probs_poly, poly.data(), sizeof(GemmProb) * n);
+  for (int k = 0; k < 3; ++k)
+    put(pl.off_tiles[k], pl.tiles[k].data(), sizeof(GemmTile) * pl.tiles[k].size());
+  for (int k = 0; k < 2; ++k) {
+    put(pl.off_probs_gram[k], gram[k].data(), sizeof(GemmProb) * n);
+    put(pl.off_probs_apply[k], apply[k].data(), sizeof(GemmProb) * n);
+  }
+  bool have_ptrs = false;
+  for (int32_t i = 0; i < n; ++i) have_ptrs |= mats[i].w != nullptr;
+  if (have_ptrs) {
+    std::vector<MatPtrs> ptrs(n);
+    for (int32_t i = 0; i < n; ++i)
+      ptrs[i] = MatPtrs{reinterpret_cast<float*>(mats[i].w), mats[i].g,
+                        reinterpret_cast<float*>(mats[i].m)};
+    put(pl.off_ptrs, ptrs.data(), sizeof(MatPtrs) * n);
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -595,119 +710,26 @@ int muonh_init(muonh_handle** out, const muonh_matrix_desc* mats, int32_t n,
       hipEventCreateWithFlags(&h->order_ev, hipEventDisableTiming) != hipSuccess)
     return bail(fail(MUONH_EHIP, "hipEventCreate failed"));
 
-  // Host images of the device tables.
-  std::vector<MatGeom> geo(n);
-  std::vector<MatScalars> scal(n);
-  std::vector<int32_t> need(n);
-  std::vector<GemmProb> gram[2], poly(n), apply[2];
-  for (int k = 0; k < 2; ++k) {
-    gram[k].resize(n);
-    apply[k].resize(n);
-  }
-  for (int32_t i = 0; i < n; ++i) {
-    const MatPlan& m = pl.mats[i];
-    MatGeom& g = geo[i];
-    g.rows = m.rows;
-    g.cols = m.cols;
-    g.tall = m.tall;
-    g.g_bf16 = m.g_bf16;
-    g.m_pad = (int32_t)m.m_pad;
-    g.n_pad = (int32_t)m.n_pad;
-    g.r_pad = (int32_t)(m.tall ? m.n_pad : m.m_pad);
-    g.c_pad = (int32_t)(m.tall ? m.m_pad : m.n_pad);
-    g.ld_skew = (int32_t)(kRowSkewBytes / pl.tsize);
-    for (int k = 0; k < 2; ++k) {
-      g.X[k] = h->ws + m.off_X[k];
-      g.XT[k] = m.off_XT[k] == kNoBuffer ? nullptr : h->ws + m.off_XT[k];
-    }
-    g.U = h->ws + m.off_U;
-    g.mom_tile0 = m.mom_tile0;
-    g.mom_ntiles = m.mom_ntiles;
-    g.chunk0 = m.chunk0;
-    g.nchunks = m.nchunks;
-    g.part0 = m.part0;
-    g.nparts = m.nparts;
-    scal[i] = MatScalars{m.radius_in > 0.0f ? (double)m.radius_in : 0.0, 0.0, 1.0f, 1.0f, 0.0f, 0.0f};
-    need[i] = m.radius_in > 0.0f ? 0 : 1;
-    const int32_t M = (int32_t)m.m_pad, N = (int32_t)m.n_pad;
-    const int32_t LM = M + g.ld_skew, LN = N + g.ld_skew;   // row pitches
-    for (int k = 0; k < 2; ++k) {
-      GemmProb& a = gram[k][i];
-      std::memset(&a, 0, sizeof(a));
-      a.P = a.Q = g.X[k];
-      a.O = h->ws + m.off_A;
-      a.M = a.N = M;
-      a.K = N;
-      a.ldp = a.ldq = LN;
-      a.ldo = LM;
-      a.um = a.un = (int32_t)m.m;
-      a.uk = (int32_t)m.n;
-      a.mat = i;
-      GemmProb& c = apply[k][i];
-      std::memset(&c, 0, sizeof(c));
-      c.P = h->ws + m.off_B;
-      c.Q = g.XT[k] ? g.XT[k] : g.X[k];   // bf16: X itself, read K-major
-      c.E = nullptr;
-      c.O = g.X[k ^ 1];
-      c.OT = g.XT[k ^ 1];
-      c.U = g.U;
-      c.M = M;
-      c.N = N;
-      c.K = M;
-      c.ldp = LM;
-      c.ldq = g.XT[k] ? LM : LN;
-      c.lde = LM;
-      c.ldo = LN;
-      c.ldot = LM;
-      c.um = (int32_t)m.m;
-      c.un = (int32_t)m.n;
-      c.uk = (int32_t)m.m;
-      c.u_tall = m.tall;
-      c.mat = i;
-      c.part0 = (int32_t)m.part0;
-    }
-    GemmProb& b = poly[i];
-    std::memset(&b, 0, sizeof(b));
-    b.P = b.Q = b.E = h->ws + m.off_A;
-    b.O = h->ws + m.off_B;
-    b.M = b.N = b.K = M;
-    b.ldp = b.ldq = b.lde = b.ldo = LM;
-    b.um = b.un = b.uk = (int32_t)m.m;
-    b.mat = i;
-  }
-  auto up = [&](size_t off, const void* src, size_t bytes) -> int {
-    if (bytes) HIP_TRY(hipMemcpy(h->ws + off, src, bytes, hipMemcpyHostToDevice));
-    return MUONH_OK;
-  };
-  if ((rc = up(pl.off_geo, geo.data(), sizeof(MatGeom) * n)) ||
-      (rc = up(pl.off_scal, scal.data(), sizeof(MatScalars) * n)) ||
-      (rc = up(pl.off_need, need.data(), sizeof(int32_t) * n)) ||
-      (rc = up(pl.off_mom_tiles, pl.mom_tiles.data(), sizeof(MomTile) * pl.mom_tiles.size())) ||
-      (rc = up(pl.off_chunks, pl.chunks.data(), sizeof(Chunk) * pl.chunks.size())) ||
-      (rc = up(pl.off_probs_poly, poly.data(), sizeof(GemmProb) * n)))
-    return bail(rc);
-  for (int k = 0; k < 3; ++k)
-    if ((rc = up(pl.off_tiles[k], pl.tiles[k].data(), sizeof(GemmTile) * pl.tiles[k].size())))
-      return bail(rc);
-  for (int k = 0; k < 2; ++k)
-    if ((rc = up(pl.off_probs_gram[k], gram[k].data(), sizeof(GemmProb) * n)) ||
-        (rc = up(pl.off_probs_apply[k], apply[k].data(), sizeof(GemmProb) * n)))
-      return bail(rc);
+  // The tables (geometry, radii, tile lists, problem descriptors, chunk
+  // tables, pointers when given) as one host image, uploaded in one copy.
+  std::vector<uint8_t> img;
+  std::vector<int32_t> need;
+  build_table_image(pl, h->ws, mats, img, need);
+  if (hipMemcpy(h->ws, img.data(), img.size(), hipMemcpyHostToDevice) != hipSuccess)
+    return bail(fail(MUONH_EHIP, "hipMemcpy of the plan tables failed"));
   // Zero the iterate / Gram buffers once so their padding starts at zero.
   const size_t big0 = pl.mats.empty() ? pl.total : pl.mats[0].off_X[0];
   if (hipMemsetAsync(h->ws + big0, 0, pl.total - big0, st) != hipSuccess)
     return bail(fail(MUONH_EHIP, "hipMemsetAsync of the workspace failed"));
 
-  // Radius R = ||W_0||_F where not given.
+  // Radius R = ||W_0||_F where not given (the image carries the pointers).
   bool any_need = false;
   for (int32_t i = 0; i < n; ++i) any_need |= need[i] != 0;
   if (any_need) {
-    std::vector<MatPtrs> ptrs(n);
+    h->cur_ptrs.resize(n);
     for (int32_t i = 0; i < n; ++i)
-      ptrs[i] = MatPtrs{reinterpret_cast<float*>(mats[i].w), mats[i].g,
-                        reinterpret_cast<float*>(mats[i].m)};
-    if ((rc = up(pl.off_ptrs, ptrs.data(), sizeof(MatPtrs) * n))) return bail(rc);
-    h->cur_ptrs = ptrs;
+      h->cur_ptrs[i] = MatPtrs{reinterpret_cast<float*>(mats[i].w), mats[i].g,
+                               reinterpret_cast<float*>(mats[i].m)};
     h->ptrs_valid = true;
     hipError_t e = launch_radius(h->at<Chunk>(pl.off_chunks), (int64_t)pl.chunks.size(),
                                  h->at<MatPtrs>(pl.off_ptrs), h->at<double>(pl.off_part_radius), st);
@@ -915,6 +937,70 @@ int muonh_step_graph(muonh_handle* h, const muonh_matrix_desc* mats, int32_t n,
   h->steps_done++;
   return MUONH_OK;
 }
+
+}  // extern "C"
+
+int muonh::run_step_in_workspace(const muonh_matrix_desc* mats, int32_t n, const muonh_options& opt,
+                                 const muonh_step_args& args, hipStream_t st, uint8_t* ws,
+                                 size_t ws_bytes, InWorkspaceHost& host) {
+  Plan P;
+  int rc = build_plan(mats, n, opt, P);
+  if (rc) return rc;
+  if (opt.workspace)
+    return fail(MUONH_EINVAL, "options.workspace must be NULL: this step uses the library's static buffer");
+  for (int32_t i = 0; i < n; ++i)
+    if (!(mats[i].radius > 0.0f))
+      return fail(MUONH_EINVAL, "matrix " + std::to_string(i) +
+                                    ": the allocation-free step needs the radius R (> 0) in the descriptor");
+  if ((rc = check_pointers(mats, n, true))) return rc;
+  if (!std::isfinite(args.elr)) return fail(MUONH_EINVAL, "elr is not finite");
+  if (args.elr_scale)
+    for (int32_t i = 0; i < n; ++i)
+      if (!std::isfinite(args.elr_scale[i])) return fail(MUONH_EINVAL, "elr_scale has a non-finite entry");
+  if (P.total > ws_bytes)
+    return fail(MUONH_ENOMEM, "the plan needs " + std::to_string(P.total) +
+                                  " bytes of workspace; the static buffer holds " +
+                                  std::to_string(ws_bytes));
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+
+  // The tables, pointers and per-matrix LR factors as one host image.  The
+  // buffer is reused across calls: wait until the device has read the
+  // previous upload from it before it is rewritten.
+  std::vector<int32_t> need;
+  std::vector<uint8_t> img;
+  build_table_image(P, ws, mats, img, need);
+  const float* scale_dev = nullptr;
+  if (args.elr_scale) {
+    std::memcpy(img.data() + P.off_elr, args.elr_scale, sizeof(float) * n);
+    scale_dev = reinterpret_cast<const float*>(ws + P.off_elr);
+  }
+  if (host.pending) {
+    HIP_TRY(hipEventSynchronize(host.uploaded));
+    host.pending = false;
+  }
+  host.img.swap(img);
+  HIP_TRY(hipMemcpyAsync(ws, host.img.data(), host.img.size(), hipMemcpyHostToDevice, st));
+  HIP_TRY(hipEventRecord(host.uploaded, st));
+  host.pending = true;
+  // The buffer keeps the previous call's contents: the Newton-Schulz
+  // buffers (whose padding must read as zero) are cleared.
+  const size_t big0 = P.mats[0].off_X[0];
+  {
+    const hipError_t e = launch_fill_zero(ws + big0, P.total - big0, st);
+    if (e != hipSuccess) return fail(MUONH_EHIP, std::string("launch_fill_zero: ") + hipGetErrorString(e));
+  }
+  // A transient handle over the region (it owns nothing).
+  muonh_handle h;
+  h.plan = std::move(P);
+  h.device = dev;
+  h.ws = ws;
+  h.last_stream = st;
+  if (const char* e = std::getenv("MUONH_DEBUG_SYNC")) h.debug_sync = std::atoi(e) != 0;
+  return enqueue_step(&h, st, step_params(h.plan, args.elr), scale_dev, nullptr);
+}
+
+extern "C" {
 
 int muonh_get_radii(muonh_handle* h, float* out, int32_t n) {
   if (!h || !out) return fail(MUONH_EINVAL, "null argument");

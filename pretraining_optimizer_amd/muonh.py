@@ -100,6 +100,9 @@ _SIGNATURES = [
                                   ctypes.POINTER(muonh_step_args), ctypes.c_void_p]),
     ("muonh_step_graph", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(muonh_matrix_desc), ctypes.c_int32,
                                         ctypes.POINTER(muonh_step_args), ctypes.c_void_p]),
+    ("muonh_step_noalloc", ctypes.c_int, [ctypes.POINTER(muonh_matrix_desc), ctypes.c_int32,
+                                          ctypes.POINTER(muonh_options), ctypes.POINTER(muonh_step_args),
+                                          ctypes.c_void_p]),
     ("muonh_get_radii", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_float), ctypes.c_int32]),
     ("muonh_get_stats", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(muonh_stats), ctypes.c_int32]),
     ("muonh_copy_update", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
@@ -327,6 +330,48 @@ class MuonH:
             self.close()
         except Exception:
             pass
+
+
+# Bytes of device workspace the allocation-free step can use per GPU (the
+# header's MUONH_NOALLOC_MAX_WORKSPACE).
+NOALLOC_MAX_WORKSPACE = 64 << 20
+
+
+def step_noalloc(weights: Sequence, moms: Sequence, grads: Sequence, radii: Sequence[float],
+                 elr: float, elr_scale: Optional[Sequence[float]] = None, step: int = 0,
+                 stream=None, **options):
+    """One MuonH step through muonh_step_noalloc: no handle, no device
+    allocation (the library's static per-GPU buffer holds the workspace).
+    weights, moms: contiguous fp32 CUDA matrices (updated in place); grads:
+    contiguous CUDA gradients (bf16 or fp32, one dtype); radii: R per matrix
+    (> 0); options: muonh_options overrides (beta, ns_dtype, ...)."""
+    lib = load_library()
+    n = len(weights)
+    if not (n and len(moms) == n and len(grads) == n and len(radii) == n):
+        raise ValueError("weights, moms, grads and radii must be non-empty lists of equal length")
+    d = (muonh_matrix_desc * n)()
+    for i, (w, m, g) in enumerate(zip(weights, moms, grads)):
+        if not (w.is_cuda and m.is_cuda and g.is_cuda) or w.dim() != 2:
+            raise ValueError(f"matrix {i}: CUDA tensors of two dims are required")
+        if w.shape != m.shape or w.shape != g.shape:
+            raise ValueError(f"matrix {i}: weight, momentum and gradient shapes differ")
+        if not (w.is_contiguous() and m.is_contiguous() and g.is_contiguous()):
+            raise ValueError(f"matrix {i}: tensors must be contiguous")
+        d[i].w, d[i].g, d[i].m = w.data_ptr(), g.data_ptr(), m.data_ptr()
+        d[i].rows, d[i].cols = w.shape
+        d[i].g_dtype = _dtype_code(g)
+        d[i].radius = float(radii[i])
+    _record(stream, list(grads) + list(weights) + list(moms))
+    opt = default_options(**options)
+    args = muonh_step_args()
+    args.elr = float(elr)
+    scale_arr = None
+    if elr_scale is not None:
+        scale_arr = (ctypes.c_float * n)(*[float(x) for x in elr_scale])
+        args.elr_scale = ctypes.cast(scale_arr, ctypes.POINTER(ctypes.c_float))
+    args.step = int(step)
+    _check(lib.muonh_step_noalloc(d, n, ctypes.byref(opt), ctypes.byref(args), _stream_ptr(stream)),
+           "muonh_step_noalloc")
 
 
 def adamw_default_options(**overrides) -> muonh_adamw_options:

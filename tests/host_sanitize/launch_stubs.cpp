@@ -45,6 +45,7 @@ hipError_t launch_finalize_radius(int32_t, const MatGeom*, const double*, const 
 hipError_t launch_copy_update(int, const void*, int64_t, float*, hipStream_t) {
   return hipErrorNoDevice;
 }
+hipError_t launch_fill_zero(void*, size_t, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_adamw(const Chunk*, int64_t, const AdamwPtrs*, AdamwParams, hipStream_t) {
   return hipErrorNoDevice;
 }

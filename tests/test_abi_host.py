@@ -214,3 +214,29 @@ def test_adamw_defaults_and_host_validation():
     assert not h.value
     assert lib.muonh_adamw_step(None, t, 2, 1e-3, 1, None) == mb.MUONH_EINVAL
     assert lib.muonh_adamw_destroy(None) == mb.MUONH_OK
+
+
+def test_noalloc_step_host_side_errors():
+    """muonh_step_noalloc rejects, before touching any device: a radius that
+    is not given, a caller workspace, and a plan larger than its static
+    buffer (MUONH_ENOMEM naming both sizes)."""
+    lib = pm.load_library()
+    assert mb.NOALLOC_MAX_WORKSPACE == 64 << 20
+    o = pm.default_options()
+    args = mb.muonh_step_args()
+    args.elr = 0.01
+    d = mb.shape_descs([(64, 96)], radius=0.0)
+    assert lib.muonh_step_noalloc(d, 1, ctypes.byref(o), ctypes.byref(args), None) == mb.MUONH_EINVAL
+    assert b"radius" in lib.muonh_last_error()
+    d = mb.shape_descs([(64, 96)], radius=3.0)
+    ow = pm.default_options()
+    ow.workspace = 256
+    assert lib.muonh_step_noalloc(d, 1, ctypes.byref(ow), ctypes.byref(args), None) == mb.MUONH_EINVAL
+    big = [(2048, 2048)] * 2
+    assert pm.workspace_size(big) > mb.NOALLOC_MAX_WORKSPACE
+    d = mb.shape_descs(big, radius=3.0)
+    assert lib.muonh_step_noalloc(d, 2, ctypes.byref(o), ctypes.byref(args), None) == mb.MUONH_ENOMEM
+    err = lib.muonh_last_error().decode()
+    assert str(pm.workspace_size(big)) in err and str(mb.NOALLOC_MAX_WORKSPACE) in err
+    assert lib.muonh_step_noalloc(None, 1, ctypes.byref(o), ctypes.byref(args), None) == mb.MUONH_EINVAL
+    assert lib.muonh_step_noalloc(d, 2, None, ctypes.byref(args), None) == mb.MUONH_EINVAL
