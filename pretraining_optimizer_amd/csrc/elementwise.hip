@@ -100,10 +100,19 @@ __device__ __forceinline__ void store4(uint16_t* p, uint16_t a, uint16_t b, uint
   st_global<u32x2_t>(p, u32x2_t{(uint32_t)a | ((uint32_t)b << 16), (uint32_t)c | ((uint32_t)d << 16)});
 }
 
+// LDS image of one momentum tile in the Newton-Schulz element type.
+//   fp32: rows of 129 elements (one padding element per row).
+//   bf16: rows of 128 elements (256 bytes) whose 8-byte units (4 columns)
+//         are XOR-swizzled by row / 4: unit u of row r sits at u ^ ((r/4) & 15).
+// With the thread layout below, each half-wavefront of the bf16 writes (one
+// 8-byte unit per lane, 32 units of one row) and of the reads (4 rows r =
+// 4i + k apart for i = 0..15, one column each) then touches every bank once,
+// where a padded linear pitch left both 2-way conflicted (two units or rows
+// per bank).
 template <typename T> struct MomLds {
-  // one padding element per row (two for 2-byte types, keeping rows 4-byte aligned)
-  static constexpr int kPitch = kMomTileC + (sizeof(T) == 2 ? 2 : 1);
+  static constexpr int kPitch = kMomTileC + (sizeof(T) == 2 ? 0 : 1);
 };
+__device__ __forceinline__ int mom_unit_swz(int r) { return (r >> 2) & 15; }
 
 template <typename T, typename G>
 __device__ __forceinline__ void momentum_tile(const MomTile& t, int64_t unit, const MatGeom& g,
@@ -165,9 +174,18 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, int64_t unit, co
         }
       }
       ss += y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
-      if (Tr)
+      if (Tr) {
+        if constexpr (sizeof(T) == 2) {
+          u32x2_t o;
+          o[0] = pack_bf16x2(y[0], y[1]);
+          o[1] = pack_bf16x2(y[2], y[3]);
+          *reinterpret_cast<u32x2_t*>(reinterpret_cast<uint8_t*>(&tile[tr_][0]) +
+                                      8 * ((cc >> 2) ^ mom_unit_swz(tr_))) = o;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tile[tr_][cc + e] = to_elem<T>(y[e]);
+          for (int e = 0; e < 4; ++e) tile[tr_][cc + e] = to_elem<T>(y[e]);
+        }
+      }
       if (D) Vec4<T>::store(D + row * ldD + col, y);
     }
   }
@@ -180,8 +198,18 @@ __device__ __forceinline__ void momentum_tile(const MomTile& t, int64_t unit, co
 #pragma unroll
     for (int q = 0; q < kMomTileC / kOpp; ++q) {
       const int oc = orow + kOpp * q;
-      store4(Tr + (c0 + oc) * ldT + r0 + oe, tile[oe][oc], tile[oe + 1][oc], tile[oe + 2][oc],
-             tile[oe + 3][oc]);
+      if constexpr (sizeof(T) == 2) {
+        // rows oe..oe+3 share one swizzle (oe is a multiple of 4)
+        const int off = 8 * ((oc >> 2) ^ mom_unit_swz(oe)) + 2 * (oc & 3);
+        const uint8_t* b = reinterpret_cast<const uint8_t*>(&tile[oe][0]) + off;
+        constexpr int kRow = MomLds<T>::kPitch * (int)sizeof(T);
+        store4(Tr + (c0 + oc) * ldT + r0 + oe, *reinterpret_cast<const T*>(b),
+               *reinterpret_cast<const T*>(b + kRow), *reinterpret_cast<const T*>(b + 2 * kRow),
+               *reinterpret_cast<const T*>(b + 3 * kRow));
+      } else {
+        store4(Tr + (c0 + oc) * ldT + r0 + oe, tile[oe][oc], tile[oe + 1][oc], tile[oe + 2][oc],
+               tile[oe + 3][oc]);
+      }
     }
   }
   // Eight wavefronts, kMomParts slots: slot w = wavefront w + wavefront w + 4.
@@ -260,7 +288,7 @@ __global__ __launch_bounds__(kMomTileThreads) void momentum_tile_kernel(const Mo
                                                                      const MatPtrs* __restrict__ ptrs,
                                                                      double* __restrict__ partials,
                                                                      ElemParams prm) {
-  __shared__ T tile[kMomTileR][MomLds<T>::kPitch];
+  __shared__ __attribute__((aligned(16))) T tile[kMomTileR][MomLds<T>::kPitch];
   const int64_t unit = first + blockIdx.x;
   const MomTile t = units[unit];
   const MatGeom& g = geo[t.mat];
