@@ -141,9 +141,10 @@ int check_pointers(const muonh_matrix_desc* mats, int32_t n, bool need_gm) {
 //   dims[p] = (M tiles, N tiles, K), upper = list only tm <= tn.
 // Units are (problem, group of up to 8 row panels); units are placed on the
 // 8 XCDs by longest-processing-time first, each XCD's units are ordered by
-// problem and group, tiles inside a unit run column-major (a column of 8
-// row tiles shares its Q panel, consecutive columns share the P panels), and
-// the per-XCD lists are interleaved so workgroup 8j + x runs XCD x's j-th tile.
+// contraction length (longest first), then problem and group, tiles inside a
+// unit run column-major (a column of 8 row tiles shares its Q panel,
+// consecutive columns share the P panels), and the per-XCD lists are
+// interleaved so workgroup 8j + x runs XCD x's j-th tile.
 std::vector<GemmTile> build_tile_list(const std::vector<std::tuple<int, int, int64_t>>& dims,
                                       bool upper) {
   struct Unit {
@@ -176,7 +177,12 @@ std::vector<GemmTile> build_tile_list(const std::vector<std::tuple<int, int, int
   std::vector<std::vector<GemmTile>> lists(kMaxXcd);
   size_t longest = 0;
   for (int x = 0; x < kMaxXcd; ++x) {
+    // Longest contraction first (then by problem and group): the XCD's CUs
+    // take tiles in list order as they free up, so short tiles fill the end
+    // of the launch instead of a long one starting last.
     std::sort(bins[x].begin(), bins[x].end(), [&](int a, int b) {
+      const int64_t ka = std::get<2>(dims[units[a].prob]), kb = std::get<2>(dims[units[b].prob]);
+      if (ka != kb) return ka > kb;
       return std::make_pair(units[a].prob, units[a].g0) < std::make_pair(units[b].prob, units[b].g0);
     });
     for (int u : bins[x]) {
