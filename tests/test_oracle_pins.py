@@ -387,3 +387,55 @@ def test_adamw_first_step_direction_is_the_sign_up_to_eps():
     d = oa.first_step_direction(g, 1e-8)
     assert d[0] == 3.0 / (3.0 + 1e-8) and d[1] == -2.0 / (2.0 + 1e-8) and d[2] == 0.0
     assert d[3] == 0.5 and d[4] == -0.5
+
+
+def _exact_ns(y_rows, steps, coeffs):
+    """The quintic iteration in exact rational arithmetic (fractions.Fraction),
+    written out with explicit sums: X_0 = Y / ||Y||_F for a Y whose Frobenius
+    norm is rational, then A = X X^T, B = b A + c A A, X = a X + B X."""
+    from fractions import Fraction
+    a, b, c = (Fraction(str(v)) for v in coeffs)
+    y = [[Fraction(v) for v in row] for row in y_rows]
+    n2 = sum(v * v for row in y for v in row)
+    # the norm is rational: find it as an exact square root
+    num, den = n2.numerator, n2.denominator
+    rn, rd = math.isqrt(num), math.isqrt(den)
+    assert rn * rn == num and rd * rd == den, "test matrix must have a rational Frobenius norm"
+    norm = Fraction(rn, rd)
+    x = [[v / norm for v in row] for row in y]
+    m, n = len(x), len(x[0])
+    for _ in range(steps):
+        A = [[sum(x[i][k] * x[j][k] for k in range(n)) for j in range(m)] for i in range(m)]
+        AA = [[sum(A[i][k] * A[k][j] for k in range(m)) for j in range(m)] for i in range(m)]
+        B = [[b * A[i][j] + c * AA[i][j] for j in range(m)] for i in range(m)]
+        x = [[a * x[i][j] + sum(B[i][k] * x[k][j] for k in range(m)) for j in range(n)] for i in range(m)]
+    return x
+
+
+@pytest.mark.parametrize("rows", [
+    [[3, 0, 4], [0, 0, 0]],                                  # 2 x 3, rank 1, ||Y|| = 5
+    [[1, -1, -2], [3, -2, 0], [1, -2, -1]],                  # 3 x 3, full rank, ||Y|| = 5
+    [[-1, -1, 1, 0, 3], [1, 3, 1, -1, -1]],                  # 2 x 5 (wide), ||Y|| = 5
+    [[2, -2, 1], [3, 1, 1], [0, 3, -2], [-1, 1, 1]],         # 4 x 3 (tall), ||Y|| = 6
+    [[3, -3, -1, -3], [3, 1, -1, 2], [-1, 0, -1, 2]],        # 3 x 4, ||Y|| = 7
+])
+def test_ns_against_exact_rational_iteration(rows):
+    """The oracle's Newton-Schulz (fp64 NumPy) against the same iteration
+    carried out exactly in rational arithmetic, on small integer matrices
+    whose Frobenius norm is an integer (eps = 0, so X_0 = Y/||Y|| exactly).
+    No floating point on the reference side: a dropped term, a wrong sign or
+    a transposed operand in the oracle shows up at O(1), while its fp64
+    rounding stays below 1e-13 relative.  The tall case is also run through
+    the oracle's orientation flip (iterating on the transpose)."""
+    y = np.array(rows, dtype=np.float64)
+    for steps in (1, 2, 5):
+        ref = _exact_ns(rows, steps, oracle.NS_COEFFS_QUINTIC)
+        ref = np.array([[float(v) for v in row] for row in ref])
+        got = oracle.newton_schulz(y, steps=steps, eps=0.0, orient=False)
+        assert np.linalg.norm(got - ref) <= 1e-13 * max(1.0, np.linalg.norm(ref)), (steps, got, ref)
+        got_o = oracle.newton_schulz(y, steps=steps, eps=0.0, orient=True)
+        assert np.linalg.norm(got_o - ref) <= 1e-12 * max(1.0, np.linalg.norm(ref)), steps
+    # the classical coefficients through the same exact route
+    ref = np.array([[float(v) for v in row] for row in _exact_ns(rows, 3, oracle.NS_COEFFS_CLASSICAL)])
+    got = oracle.newton_schulz(y, steps=3, coeffs=oracle.NS_COEFFS_CLASSICAL, eps=0.0, orient=False)
+    assert np.linalg.norm(got - ref) <= 1e-13 * max(1.0, np.linalg.norm(ref))
