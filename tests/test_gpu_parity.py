@@ -432,6 +432,36 @@ def test_nesterov_and_elr_scale_and_resume_radius(tile, monkeypatch):
     check_reports(reps, TOL_F32, [0.02, 0.02])
 
 
+@pytest.mark.parametrize("ns,steps,coeffs,beta", [
+    ("f32", 1, "quintic", 0.95), ("bf16", 1, "quintic", 0.95),
+    ("f32", 2, "quintic", 0.95), ("bf16", 3, "quintic", 0.95),
+    ("bf16", 8, "quintic", 0.95), ("f32", 5, "classical", 0.9),
+    ("bf16", 4, "classical", 0.9),
+])
+@pytest.mark.parametrize("tile", ["auto", "256"])
+def test_iteration_count_and_coefficients(ns, steps, coeffs, beta, tile, monkeypatch):
+    """The options the ABI takes beside the defaults: other Newton-Schulz
+    iteration counts (one iteration makes a single B'X launch both the first,
+    which applies the normalisation, and the last, which writes u and the
+    update statistics; odd and even counts end in different iterate
+    buffers), the classical cubic-equivalent coefficients (15/8, -10/8, 3/8)
+    and another momentum coefficient, against the oracle with the same
+    options (a plain reading of the iteration the arXiv page's Section 3.3
+    update wraps, whatever its length)."""
+    if tile != "auto":
+        monkeypatch.setenv("MUONH_GEMM_TILE", tile)
+    announce(f"{steps} NS steps, {coeffs} coefficients, beta {beta}, {ns} NS, GEMM tile {tile}")
+    shapes = [(300, 512), (640, 256), (256, 256), (129, 1000)]
+    mw, mg = _gauss_fns(shapes, torch.bfloat16 if ns == "bf16" else torch.float32, seed=17 + steps)
+    oo = oracle.OracleOptions(
+        beta=beta, ns_steps=steps,
+        ns_coeffs=oracle.NS_COEFFS_QUINTIC if coeffs == "quintic" else oracle.NS_COEFFS_CLASSICAL)
+    etas = [0.03, 0.02]
+    reps = run_parity(shapes, mw, mg, etas, check=list(range(len(shapes))), ns=ns, oracle_opts=oo)
+    summarize(f"{steps} NS steps, {coeffs}, beta {beta}, {ns}, tile {tile}", reps)
+    check_reports(reps, TOL_BF16 if ns == "bf16" else TOL_F32, etas)
+
+
 @pytest.mark.parametrize("tile", ["auto", "256"])
 def test_resume_from_saved_state_is_bitwise(tile, monkeypatch):
     """All state is the caller's (W, M) plus the radii: 3 steps, a new handle
