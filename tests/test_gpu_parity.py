@@ -435,7 +435,7 @@ def test_nesterov_and_elr_scale_and_resume_radius(tile, monkeypatch):
 @pytest.mark.parametrize("ns,steps,coeffs,beta", [
     ("f32", 1, "quintic", 0.95), ("bf16", 1, "quintic", 0.95),
     ("f32", 2, "quintic", 0.95), ("bf16", 3, "quintic", 0.95),
-    ("bf16", 8, "quintic", 0.95), ("f32", 5, "classical", 0.9),
+    ("bf16", 6, "quintic", 0.95), ("f32", 5, "classical", 0.9),
     ("bf16", 4, "classical", 0.9),
 ])
 @pytest.mark.parametrize("tile", ["auto", "256"])
