@@ -13,7 +13,8 @@
 //  - order: within an XCD's share, the contraction length never increases
 //    (longest first);
 //  - the executed-FLOP count of the plan equals the sum over listed tiles;
-//  - the small-problem path lists each 64 x 64 tile of the valid dims once.
+//  - the small-problem path lists each 64 x 64 tile of the valid dims once;
+//  - the momentum-unit, chunk and partial-slot tables (check_tables).
 // Prints "all checks passed" and exits 0, or exits 1 at the first failure.
 #include "../../pretraining_optimizer_amd/csrc/muonh.cpp"
 
@@ -137,6 +138,48 @@ int check_small(const Plan& P, const std::string& name) {
   return 0;
 }
 
+// The per-matrix tables the elementwise kernels and the finalisers index:
+// momentum units (row segments of the padded grid when X_0 keeps M's
+// orientation in the bf16 plan, 64 x 128 tiles otherwise) contiguous from the
+// matrix's first unit and covering its padded grid once, row units before
+// tile units; flat chunks covering its elements in order; and the partial
+// slots of the last B'X launch laid out back to back.
+int check_tables(const Plan& P, const std::string& name) {
+  const char* what = name.c_str();
+  int64_t part = 0;
+  for (int32_t i = 0; i < P.n; ++i) {
+    const auto& m = P.mats[i];
+    const int64_t r_pad = m.tall ? m.n_pad : m.m_pad, c_pad = m.tall ? m.m_pad : m.n_pad;
+    const bool rows = P.bf16 && !m.tall;
+    const int64_t nseg = (c_pad + kMomRowSeg - 1) / kMomRowSeg;
+    const int64_t want = rows ? r_pad * nseg : (r_pad / kMomTileR) * (c_pad / kMomTileC);
+    CHECK(m.mom_ntiles == want, what);
+    CHECK(m.mom_tile0 >= 0 && m.mom_tile0 + m.mom_ntiles <= (int64_t)P.mom_tiles.size(), what);
+    CHECK(rows ? m.mom_tile0 + m.mom_ntiles <= P.mom_rows : m.mom_tile0 >= P.mom_rows, what);
+    std::set<std::pair<int, int>> seen;
+    for (int64_t j = m.mom_tile0; j < m.mom_tile0 + m.mom_ntiles; ++j) {
+      const MomTile& u = P.mom_tiles[j];
+      CHECK(u.mat == i && u.kind == (rows ? 1 : 0), what);
+      CHECK(u.tr >= 0 && u.tc >= 0, what);
+      CHECK(rows ? (u.tr < r_pad && u.tc < nseg) : (u.tr < r_pad / kMomTileR && u.tc < c_pad / kMomTileC), what);
+      CHECK(seen.insert({u.tr, u.tc}).second, what);
+    }
+    const int64_t elems = m.rows * m.cols;
+    CHECK(m.nchunks == (elems + kChunk - 1) / kChunk, what);
+    for (int64_t j = 0; j < m.nchunks; ++j) {
+      const Chunk& c = P.chunks[m.chunk0 + j];
+      CHECK(c.mat == i && c.start == j * kChunk && c.len == std::min<int64_t>(kChunk, elems - c.start), what);
+    }
+    CHECK(m.part0 == part, what);
+    part += m.nparts;
+  }
+  CHECK(part == P.nparts, what);
+  int64_t units = 0, chunks = 0;
+  for (const auto& m : P.mats) units += m.mom_ntiles, chunks += m.nchunks;
+  CHECK(units == (int64_t)P.mom_tiles.size() && chunks == (int64_t)P.chunks.size(), what);
+  return 0;
+}
+
 }  // namespace
 
 int main() {
@@ -173,6 +216,7 @@ int main() {
           return 1;
         }
         if ((P.small_gemm ? check_small(P, tag) : check_big(P, tag)) != 0) return 1;
+        if (check_tables(P, tag) != 0) return 1;
         ++plans;
         small += P.small_gemm;
       }
