@@ -137,10 +137,11 @@ def kernel_source_sha() -> str:
     return h.hexdigest()
 
 
-def traffic_for(kernel: str):
+def traffic_for(kernel: str, workload: str, ns: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     profile (FETCH_SIZE and WRITE_SIZE runs, calibrated against a plain copy),
-    or None when there is none or the kernel sources changed since."""
+    or None when there is none for this kernel, workload and Newton-Schulz
+    type, or the kernel sources changed since."""
     try:
         with open(TRAFFIC_PROFILE) as f:
             lines = f.read().splitlines()
@@ -151,7 +152,8 @@ def traffic_for(kernel: str):
         if line.startswith("- ") and ": " in line:
             k, v = line[2:].split(": ", 1)
             kv[k.strip()] = v.strip().strip("`")
-    if kv.get("kernel-source-sha256") != kernel_source_sha() or kv.get("kernel") != kernel:
+    if (kv.get("kernel-source-sha256") != kernel_source_sha() or kv.get("kernel") != kernel
+            or kv.get("workload") != workload or kv.get("ns-dtype") != ns):
         return None
     return float(kv["hbm-bytes-per-launch"])
 
@@ -428,7 +430,7 @@ def main():
         names = {k: v.replace("<bf16", "<fp32") for k, v in names.items()}
     dom = max((k for k in kern if k in names), key=lambda k: per_step[k])
     roof = {"bound": "mfma", "achieved": kern[dom]["alg_tflops"], "peak": peak, "unit": "TFLOP/s",
-            "frac": kern[dom]["alg_tflops"] / peak, "traffic": traffic_for(dom),
+            "frac": kern[dom]["alg_tflops"] / peak, "traffic": traffic_for(dom, wl.name, ns),
             "kernel": names[dom], "flop_per_launch": fl_alg[dom] / launches[dom],
             "ms_per_launch": kern[dom]["ms_per_launch"]}
 

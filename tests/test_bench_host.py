@@ -90,4 +90,14 @@ def test_traffic_key_ignores_comments_only(tmp_path, monkeypatch):
 
 def test_traffic_is_none_when_the_key_does_not_match(monkeypatch):
     monkeypatch.setattr(bench, "kernel_source_sha", lambda: "0" * 64)
-    assert bench.traffic_for("ns_apply") is None
+    assert bench.traffic_for("ns_apply", "qwen3_1.7b", "bf16") is None
+
+
+def test_traffic_belongs_to_its_kernel_workload_and_type():
+    """The committed counter profile covers the bf16 B'X launch of the 1.7B
+    set only: another workload, Newton-Schulz type or kernel gets None."""
+    t = bench.traffic_for("ns_apply", "qwen3_1.7b", "bf16")
+    assert t is not None and t > 0
+    assert bench.traffic_for("ns_apply", "diag170m", "bf16") is None
+    assert bench.traffic_for("ns_apply", "qwen3_1.7b", "f32") is None
+    assert bench.traffic_for("ns_gram", "qwen3_1.7b", "bf16") is None
