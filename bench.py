@@ -107,14 +107,19 @@ def exec_flops(shapes, ns_steps, tsize, small: bool, symmetric: bool = True):
     return out
 
 
-def plan_exec_flops(shapes, ns_steps, tsize, plan_total):
-    """exec_flops on the GEMM path the library's plan took (the one whose
-    total equals the plan's executed FLOP)."""
+def plan_gemm_path(shapes, ns_steps, tsize, plan_total):
+    """(exec_flops, small) on the GEMM path the library's plan took: the one
+    whose total equals the plan's executed FLOP (small: the 64 x 64 path)."""
     for small in (False, True):
         ex = exec_flops(shapes, ns_steps, tsize, small)
         if abs(sum(ex.values()) - plan_total) <= 1e-9 * max(plan_total, 1.0):
-            return ex
+            return ex, small
     raise RuntimeError("the executed-FLOP model matches neither GEMM path of the plan")
+
+
+def plan_exec_flops(shapes, ns_steps, tsize, plan_total):
+    """exec_flops on the GEMM path the library's plan took."""
+    return plan_gemm_path(shapes, ns_steps, tsize, plan_total)[0]
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_apply_qwen3_1.7b_traffic.md")
@@ -384,7 +389,7 @@ def main():
     #   exec:  the MFMA FLOP the grouped GEMM issues (padding, upper tiles);
     #   dense: the dense-equivalent count (2 m^2 n, 2 m^3, 2 m^2 n).
     launches = {"ns_gram": S, "ns_poly": S, "ns_apply": S - 1, "ns_apply_last": 1}
-    ex = plan_exec_flops(wl.shapes, S, tsize, info.ns_exec_flops)
+    ex, small_path = plan_gemm_path(wl.shapes, S, tsize, info.ns_exec_flops)
     last = {"ns_gram": 1.0, "ns_poly": 1.0, "ns_apply": (S - 1) / S, "ns_apply_last": 1.0 / S}
     src = {"ns_gram": "ns_gram", "ns_poly": "ns_poly", "ns_apply": "ns_apply", "ns_apply_last": "ns_apply"}
     half = {"ns_gram": 0.5, "ns_poly": 0.5, "ns_apply": 1.0, "ns_apply_last": 1.0}
@@ -428,6 +433,8 @@ def main():
              "ns_apply_last": "gemm_kernel<bf16, kApplyLast> (u = B' X)"}
     if ns != "bf16":
         names = {k: v.replace("<bf16", "<fp32") for k, v in names.items()}
+    if small_path:
+        names = {k: v.replace("gemm_kernel<", "gemm_small_kernel<") for k, v in names.items()}
     dom = max((k for k in kern if k in names), key=lambda k: per_step[k])
     roof = {"bound": "mfma", "achieved": kern[dom]["alg_tflops"], "peak": peak, "unit": "TFLOP/s",
             "frac": kern[dom]["alg_tflops"] / peak, "traffic": traffic_for(dom, wl.name, ns),

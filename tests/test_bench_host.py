@@ -53,6 +53,11 @@ def test_executed_and_floor_flop_models_match_the_plan(monkeypatch):
     # the single 256 x 128 matrix runs on the 64 x 64 path
     info = pm.plan_query([(256, 128)], pm.default_options(ns_dtype=pm.MUONH_F32), g_dtype=pm.MUONH_F32)
     assert sum(bench.exec_flops([(256, 128)], 5, 4, True).values()) == pytest.approx(info.ns_exec_flops)
+    # ... and bench names the kernel of the path the plan took
+    assert bench.plan_gemm_path([(256, 128)], 5, 4, info.ns_exec_flops)[1] is True
+    wl = inputs.workload("qwen3_1.7b")
+    big = pm.plan_query(wl.shapes, pm.default_options(ns_dtype=pm.MUONH_BF16))
+    assert bench.plan_gemm_path(wl.shapes, 5, 2, big.ns_exec_flops)[1] is False
     monkeypatch.setenv("MUONH_GEMM_TILE", "256")
     info = pm.plan_query([(256, 128)], pm.default_options(ns_dtype=pm.MUONH_F32), g_dtype=pm.MUONH_F32)
     assert sum(bench.exec_flops([(256, 128)], 5, 4, False).values()) == pytest.approx(info.ns_exec_flops)
