@@ -107,6 +107,14 @@ def exec_flops(shapes, ns_steps, tsize, small: bool, symmetric: bool = True):
     return out
 
 
+def synthetic_data_label(wl) -> str:
+    """The `data` field: how the workload's synthetic inputs are drawn."""
+    grads = {"normal": "N(0,1) grads",
+             "fan_in": "N(0,1)/sqrt(fan_in) grads",
+             "lowrank": "rank-8 signal (singular values 10^U(-3,1)) plus N(0,1e-3) noise grads"}
+    return f"synthetic (seeded {grads[wl.grad_kind]}, W_0 at Frobenius norm sqrt(rows))"
+
+
 def plan_gemm_path(shapes, ns_steps, tsize, plan_total):
     """(exec_flops, small) on the GEMM path the library's plan took: the one
     whose total equals the plan's executed FLOP (small: the 64 x 64 path)."""
@@ -458,7 +466,7 @@ def main():
         "metric": METRIC, "value": steps_per_s, "unit": "steps/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": ns, "data": "synthetic (seeded N(0,1) grads, W at radius sqrt(rows))",
+        "dtype": ns, "data": synthetic_data_label(wl),
         "config": {"workload": f"{wl.name}: {len(wl.shapes)} matrices, {params} params, fp32 W/M, "
                                f"{'bf16' if gsize == 2 else 'fp32'} grads, {ns} Newton-Schulz x{S}",
                    "matrices": len(wl.shapes), "params": params, "parallelism": "single-gpu"},

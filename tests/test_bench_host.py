@@ -106,3 +106,9 @@ def test_traffic_belongs_to_its_kernel_workload_and_type():
     assert bench.traffic_for("ns_apply", "diag170m", "bf16") is None
     assert bench.traffic_for("ns_apply", "qwen3_1.7b", "f32") is None
     assert bench.traffic_for("ns_gram", "qwen3_1.7b", "bf16") is None
+
+
+def test_data_label_follows_the_workload():
+    assert "N(0,1) grads" in bench.synthetic_data_label(inputs.workload("qwen3_1.7b"))
+    assert "fan_in" in bench.synthetic_data_label(inputs.workload("diag170m"))
+    assert "rank-8" in bench.synthetic_data_label(inputs.workload("stress"))
